@@ -1,0 +1,167 @@
+/*
+ * snr_oracle.c - scalar double-precision reference for row-wise RMSNorm and
+ * the fused dual-epsilon sandwich tail.
+ *
+ * TEST INFRASTRUCTURE ONLY. The library's compute path never links, loads or
+ * calls this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do. It includes no header of the HIP library and shares no
+ * source, table or helper with it.
+ *
+ * Every quantity is evaluated in IEEE-754 double precision by plain loops in
+ * index order, with no blocking, fusion or reordering, so that each function
+ * can be checked against the definitions by eye. Inputs arrive as f32 values
+ * (or bf16 bit patterns) and are widened to double exactly; epsilon arrives as
+ * the f32 value the GPU library receives and is widened exactly as well.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (no FMA contraction, so every product and sum is rounded once, as written).
+ *
+ * Every function here is pinned by tests/test_oracle_pins.py against values
+ * the pages print, closed forms, invariants, library routines and exact
+ * rational arithmetic; tests/test_oracle_mutants.py shows that plausible
+ * mistakes planted in a copy of this file fail those pins.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EBADARG 1
+
+/* Exact bf16 -> f32 widening: a bf16 value is the top half of an f32. */
+static float bf16_bits_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/*
+ * One row of RMSNorm, following "RMSNorm and the dual-epsilon sandwich"
+ * (Muser book ch. 12), section 12.1 "What it computes":
+ *   mean(x^2) = (1/n) * sum_j x_j^2
+ *   rms       = sqrt(mean(x^2) + eps)        (eps inside the root)
+ *   y_i       = x_i / rms * gamma_i
+ * The same three steps are the algorithm listed for Hesper's rmsNormKernel
+ * ("Hesper.Layers.RMSNorm", GPU Kernel Implementation: RMS = sqrt(sum/n + eps),
+ * then y = x / RMS * scale).
+ * Returns rms (the denominator) so callers can inspect it.
+ */
+static double rms_row(const double *x, const double *gamma, double eps,
+                      int64_t n, double *y)
+{
+    double sum_sq = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        sum_sq += x[j] * x[j];
+    const double mean_sq = sum_sq / (double)n;
+    const double rms = sqrt(mean_sq + eps);
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = x[j] / rms * gamma[j];
+    return rms;
+}
+
+/*
+ * Plain RMSNorm over `rows` contiguous rows of length n, f32 inputs.
+ * y: rows*n doubles. rms_out: optional (NULL) array of `rows` denominators.
+ * Scratch for the widened row and gamma is provided by the caller through
+ * `work` (2*n doubles) so that this file performs no allocation.
+ */
+int snr_oracle_rmsnorm_f32(const float *x, const float *gamma, float eps,
+                           int64_t rows, int64_t n, double *y,
+                           double *rms_out, double *work)
+{
+    if (n < 1 || rows < 0 || !x || !gamma || !y || !work)
+        return ORACLE_EBADARG;
+    double *xr = work, *gr = work + n;
+    for (int64_t j = 0; j < n; ++j)
+        gr[j] = (double)gamma[j];
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            xr[j] = (double)x[i * n + j];
+        const double rms = rms_row(xr, gr, (double)eps, n, y + i * n);
+        if (rms_out)
+            rms_out[i] = rms;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Plain RMSNorm with bf16 storage: x and gamma are bf16 bit patterns, decoded
+ * exactly to f32 and then to double; the result is the exact-input definition
+ * in double (no output rounding, which is the GPU's business).
+ */
+int snr_oracle_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma,
+                            float eps, int64_t rows, int64_t n, double *y,
+                            double *rms_out, double *work)
+{
+    if (n < 1 || rows < 0 || !x || !gamma || !y || !work)
+        return ORACLE_EBADARG;
+    double *xr = work, *gr = work + n;
+    for (int64_t j = 0; j < n; ++j)
+        gr[j] = (double)bf16_bits_to_f32(gamma[j]);
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            xr[j] = (double)bf16_bits_to_f32(x[i * n + j]);
+        const double rms = rms_row(xr, gr, (double)eps, n, y + i * n);
+        if (rms_out)
+            rms_out[i] = rms;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The dual-epsilon sandwich tail, one row at a time. It follows the sandwich
+ * order of "RMSNorm and the dual-epsilon sandwich", section 12.2 (post-norm on
+ * the sub-block output before the residual add, then the next pre-norm on the
+ * updated stream), and the fused tail of section 12.4.3:
+ *   hidden += rms_norm(src, eps1) * weight1
+ *   output  = rms_norm(hidden, eps2) * weight2
+ * With a = src (sub-block output), r = the residual stream before the add:
+ *   d_a = sqrt(mean(a^2) + eps_post)
+ *   p_j = a_j / d_a * gamma_post_j           (post-norm output)
+ *   h_j = r_j + p_j                          (residual add; updated stream)
+ *   d_h = sqrt(mean(h^2) + eps_pre)
+ *   y_j = h_j / d_h * gamma_pre_j            (next block's pre-normed input)
+ * Hesper's residualAddRmsNormKernel (write both the sum and its norm) is the
+ * second half of the same chain. h is kept in double: it is NOT rounded to f32
+ * before the second norm.
+ *
+ * Outputs (all rows*n or rows doubles): h, y; optional p (post-norm term),
+ * d_a, d_h (the two denominators). `work` holds 4*n doubles.
+ */
+int snr_oracle_sandwich_tail(const float *a, const float *r,
+                             const float *gamma_post, float eps_post,
+                             const float *gamma_pre, float eps_pre,
+                             int64_t rows, int64_t n, double *h, double *y,
+                             double *p_out, double *d_a_out, double *d_h_out,
+                             double *work)
+{
+    if (n < 1 || rows < 0 || !a || !r || !gamma_post || !gamma_pre || !h ||
+        !y || !work)
+        return ORACLE_EBADARG;
+    double *ar = work, *p = work + n, *gp = work + 2 * n, *gq = work + 3 * n;
+    for (int64_t j = 0; j < n; ++j) {
+        gp[j] = (double)gamma_post[j];
+        gq[j] = (double)gamma_pre[j];
+    }
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            ar[j] = (double)a[i * n + j];
+        /* post-norm of the sub-block output, epsilon eps_post */
+        const double d_a = rms_row(ar, gp, (double)eps_post, n, p);
+        /* residual add */
+        double *hi = h + i * n;
+        for (int64_t j = 0; j < n; ++j)
+            hi[j] = (double)r[i * n + j] + p[j];
+        /* next pre-norm of the updated stream, epsilon eps_pre */
+        const double d_h = rms_row(hi, gq, (double)eps_pre, n, y + i * n);
+        if (p_out)
+            memcpy(p_out + i * n, p, (size_t)n * sizeof(double));
+        if (d_a_out)
+            d_a_out[i] = d_a;
+        if (d_h_out)
+            d_h_out[i] = d_h;
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for RMSNorm and the dual-epsilon sandwich tail.
+
+This module is shared by the GPU path's tests and benchmark and by the oracle's
+tests. It draws random numbers and lays out arrays; it contains none of the
+method's arithmetic (no mean of squares, no epsilon, no normalisation).
+
+The workloads stand in for the residual stream of the model the Muser book
+describes (hidden width n = 6656, section 12.1 of "RMSNorm and the
+dual-epsilon sandwich"): real activations need that model's weights, which are
+not available, so each configuration draws Gaussian rows with a log-uniform
+per-row scale, and per-channel gains gamma = 1 + 0.1 * N(0, 1).
+
+Every array comes from ``numpy.random.Generator(PCG64(seed))``; the order of
+draws within a configuration is fixed, so a seed names the data exactly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F32 = np.float32
+
+
+def rng_for(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# -- bf16 storage helpers (encode for input preparation, exact decode) -------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even) and return
+    the 16-bit patterns as uint16. NaN stays NaN (quietened)."""
+    u = np.ascontiguousarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    r = np.where(nan, ((u >> 16) | 0x40) & 0xFFFF, r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(F32)
+
+
+# -- configurations ------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    kind: str            # "plain" or "tail"
+    rows: int
+    n: int
+    dtype: str           # "f32" or "bf16" (storage type)
+    seed: int
+    eps: tuple           # (eps,) for plain; (eps_post, eps_pre) for tail
+    scale_exp: tuple = ()   # per-row log10 scale range(s)
+    edge: bool = False   # structured rows 0-5 + log-uniform mean-square
+    notes: str = field(default="", compare=False)
+
+
+EPS_PRE = 1e-5    # pre-norm epsilon (the checkpoint's value)
+EPS_POST = 1e-8   # post-norm epsilon (hard-coded in the sandwich's post norms)
+
+EDGE_NS = (2, 3, 768, 2048, 6657, 16384, 65536)
+
+
+def _configs() -> dict:
+    c = {}
+
+    def add(cfg: Config):
+        c[cfg.name] = cfg
+
+    add(Config("plain_64x6656_f32", "plain", 64, 6656, "f32", 101, (1e-5,),
+               ((-2.0, 1.0),)))
+    add(Config("tail_1x6656_f32", "tail", 1, 6656, "f32", 201,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("tail_8x6656_f32", "tail", 8, 6656, "f32", 208,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("tail_4096x6656_f32", "tail", 4096, 6656, "f32", 301,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("plain_16384x4096_bf16", "plain", 16384, 4096, "bf16", 401,
+               (1e-6,), ((-2.0, 2.0),)))
+    for n in EDGE_NS:
+        add(Config(f"edge_256x{n}_f32", "plain", 256, n, "f32", 500 + n,
+                   (1e-5,), ((-12.0, 6.0),), edge=True))
+    return c
+
+
+CONFIGS = _configs()
+HEADLINE = "tail_4096x6656_f32"
+
+
+def _gamma(rng: np.random.Generator, n: int) -> np.ndarray:
+    return (1.0 + 0.1 * rng.standard_normal(n)).astype(F32)
+
+
+def _scaled_normal(rng, rows, n, lo, hi) -> np.ndarray:
+    """Rows of N(0,1) times a per-row scale 10**U(lo, hi)."""
+    scale = 10.0 ** rng.uniform(lo, hi, rows)
+    z = rng.standard_normal((rows, n))
+    z *= scale[:, None]
+    return z.astype(F32)
+
+
+def _edge_rows(rng, rows, n, lo, hi) -> np.ndarray:
+    """Edge-sweep rows: row i has target mean-square m_i = 10**U(lo, hi), drawn
+    as N(0,1) * sqrt(m_i) (so E[mean(x^2)] = m_i). Rows 0-5 are structured:
+    all zero, constant +c, constant -c, alternating +-c, a one-hot spike, and a
+    row at the smallest target mean-square 10**lo."""
+    m = 10.0 ** rng.uniform(lo, hi, rows)
+    z = rng.standard_normal((rows, n))
+    z *= np.sqrt(m)[:, None]
+    x = z.astype(F32)
+    c = 1.5
+    if rows > 0:
+        x[0] = 0.0
+    if rows > 1:
+        x[1] = c
+    if rows > 2:
+        x[2] = -c
+    if rows > 3:
+        x[3] = np.where(np.arange(n) % 2 == 0, c, -c)
+    if rows > 4:
+        x[4] = 0.0
+        x[4, n // 2] = 100.0
+    if rows > 5:
+        x[5] = (rng.standard_normal(n) * np.sqrt(10.0 ** lo)).astype(F32)
+    return x
+
+
+def make_plain(cfg: Config, rows: int | None = None) -> dict:
+    """Inputs for a plain RMSNorm configuration. ``rows`` may shrink the row
+    count (the first rows of the same stream are NOT guaranteed identical to
+    the full draw; a smaller row count is its own seeded input)."""
+    assert cfg.kind == "plain"
+    rows = cfg.rows if rows is None else rows
+    rng = rng_for(cfg.seed)
+    gamma = _gamma(rng, cfg.n)
+    lo, hi = cfg.scale_exp[0]
+    if cfg.edge:
+        x = _edge_rows(rng, rows, cfg.n, lo, hi)
+    else:
+        x = _scaled_normal(rng, rows, cfg.n, lo, hi)
+    out = {"x": x, "gamma": gamma, "eps": cfg.eps[0]}
+    if cfg.dtype == "bf16":
+        out["x"] = f32_to_bf16_bits(x)
+        out["gamma"] = f32_to_bf16_bits(gamma)
+    return out
+
+
+def make_tail(cfg: Config, rows: int | None = None) -> dict:
+    """Inputs for a sandwich-tail configuration: block output a, residual r,
+    the two gains and the two epsilons."""
+    assert cfg.kind == "tail"
+    rows = cfg.rows if rows is None else rows
+    rng = rng_for(cfg.seed)
+    gamma_post = _gamma(rng, cfg.n)
+    gamma_pre = _gamma(rng, cfg.n)
+    (alo, ahi), (rlo, rhi) = cfg.scale_exp
+    a = _scaled_normal(rng, rows, cfg.n, alo, ahi)
+    r = _scaled_normal(rng, rows, cfg.n, rlo, rhi)
+    return {"a": a, "r": r, "gamma_post": gamma_post, "gamma_pre": gamma_pre,
+            "eps_post": cfg.eps[0], "eps_pre": cfg.eps[1]}
+
+
+def make(cfg_or_name, rows: int | None = None) -> dict:
+    cfg = CONFIGS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
+    return make_plain(cfg, rows) if cfg.kind == "plain" else make_tail(cfg, rows)
+
+
+def random_plain(rows: int, n: int, seed: int, lo: float = -3.0,
+                 hi: float = 3.0, dtype: str = "f32") -> dict:
+    """Ad-hoc plain inputs for shape sweeps (same recipe as the configs)."""
+    cfg = Config(f"adhoc_{rows}x{n}", "plain", rows, n, dtype, seed, (1e-5,),
+                 ((lo, hi),))
+    return make_plain(cfg)
+
+
+def random_tail(rows: int, n: int, seed: int) -> dict:
+    """Ad-hoc tail inputs for shape sweeps (same recipe as the configs)."""
+    cfg = Config(f"adhoc_tail_{rows}x{n}", "tail", rows, n, "f32", seed,
+                 (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0)))
+    return make_tail(cfg)

@@ -1,0 +1,397 @@
+"""Pins that tie the f64 oracle to something other than itself.
+
+Each ``pin_*`` function takes a loaded oracle handle and raises
+AssertionError (or any exception) if the oracle disagrees with:
+
+* the values the Muser book prints for its worked example (section 12.3 of
+  "RMSNorm and the dual-epsilon sandwich", Figure 12.1; golden file
+  ``golden/rmsnorm_worked_example.txt``);
+* closed forms that follow from the definition in section 12.1 (constant rows,
+  n = 1 and n = 2 rows, zero rows, epsilon-dominated rows);
+* invariants (mean of y^2 with unit gain, scale invariance under powers of two,
+  row independence);
+* library routines: ``torch.nn.functional.rms_norm`` in f64 (one of the public
+  references the dormouse report uses) and, on exactly mean-centred rows,
+  ``torch.nn.functional.layer_norm`` (section 12.2: mean(x^2) = var + mean^2,
+  so the two coincide when the mean is zero);
+* exact rational arithmetic (Python ``decimal`` at 50 digits) on tiny inputs,
+  for the plain norm in f32 and bf16 storage and for the fused tail, with rows
+  sized so that both epsilons of the tail matter.
+
+The functions are plain callables so that ``test_oracle_mutants.py`` can run
+the same pins against deliberately broken copies of the oracle.
+"""
+from __future__ import annotations
+
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+from sandwich_norm_residual_amd.inputs import (bf16_bits_to_f32,
+                                                f32_to_bf16_bits, rng_for)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F32 = np.float32
+
+
+def _f(v) -> float:
+    """The exact double value of an f32 scalar."""
+    return float(np.float32(v))
+
+
+def read_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, vals, tol = (s.strip() for s in line.split("|"))
+            out[key] = (np.array([float(v) for v in vals.split()]), float(tol))
+    return out
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.maximum(np.abs(b), 1e-300)
+    return np.where(b == 0, np.abs(a), np.abs(a - b) / den)
+
+
+# ---------------------------------------------------------------------------
+# Page-printed values
+# ---------------------------------------------------------------------------
+
+def pin_worked_example(O):
+    g = read_golden("rmsnorm_worked_example.txt")
+    x = g["x"][0].astype(F32)[None, :]
+    eps = float(g["eps"][0][0])
+    for gkey, ykey in (("gamma_one", "y_one"), ("gamma_two", "y_two")):
+        gamma = g[gkey][0].astype(F32)
+        y, rms = O.rmsnorm(x, gamma, eps, return_rms=True)
+        want, tol = g[ykey]
+        assert np.all(np.abs(y[0] - want) <= tol), (ykey, y[0], want)
+        zero = want == 0
+        assert np.all(y[0][zero] == 0.0), "zeros of the example must be exact"
+        r, rtol = g["rms"]
+        assert abs(rms[0] - r[0]) <= rtol, ("rms", rms[0])
+        inv, itol = g["inv_rms"]
+        assert abs(1.0 / rms[0] - inv[0]) <= itol, ("inv_rms", 1 / rms[0])
+    y1 = O.rmsnorm(x, g["gamma_one"][0].astype(F32), eps)
+    m, mtol = g["mean_y_sq"]
+    assert abs(np.mean(y1[0] ** 2) - m[0]) <= mtol
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def pin_constant_rows(O):
+    """x = c everywhere: mean(x^2) = c^2, so y_j = gamma_j c / sqrt(c^2 + eps)."""
+    rng = rng_for(11)
+    for n in (1, 2, 3, 7, 100, 1000):
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        for c in (1.5, -1.5, 3.0e-4, -7.0e3, 2.0 ** -20, 1e18):
+            for eps in (1e-5, 1e-8, 1e-6):
+                x = np.full((1, n), c, F32)
+                y = O.rmsnorm(x, gamma, eps)[0]
+                cf, ef = _f(c), _f(eps)
+                want = gamma.astype(np.float64) * (cf / math.sqrt(cf * cf + ef))
+                # f64 sequential sum of n equal squares: relative error of the
+                # sum <= (n - 1) u, halved by the root, plus a few roundings
+                bound = (n + 8) * 2.0 ** -53
+                assert np.max(_rel(y, want)) < bound, (n, c, eps)
+
+
+def pin_zero_rows(O):
+    """A zero row normalises to exactly zero (eps keeps the root positive);
+    in the tail, a = 0 or gamma_post = 0 leaves h = r exactly."""
+    rng = rng_for(12)
+    for n in (1, 2, 5, 64):
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        y = O.rmsnorm(np.zeros((3, n), F32), gamma, 1e-5)
+        assert np.all(y == 0.0) and np.all(np.isfinite(y))
+        r = rng.standard_normal((2, n)).astype(F32)
+        a = rng.standard_normal((2, n)).astype(F32)
+        gq = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        plain_r = O.rmsnorm(r, gq, 1e-5)
+        for aa, gp in ((np.zeros_like(a), gamma), (a, np.zeros(n, F32))):
+            t = O.sandwich_tail(aa, r, gp, 1e-8, gq, 1e-5)
+            assert np.array_equal(t.h, r.astype(np.float64))
+            assert np.array_equal(t.p, np.zeros_like(t.p))
+            assert np.max(_rel(t.y, plain_r)) < 1e-15
+
+
+def pin_n1(O):
+    """n = 1: y = gamma x / sqrt(x^2 + eps)."""
+    for xv in (0.5, -3.0, 1e-4, 1e-3, 123.25):
+        for eps in (1e-5, 1e-8):
+            y = O.rmsnorm(np.array([[xv]], F32), np.array([0.75], F32), eps)
+            xf = _f(xv)
+            want = 0.75 * xf / math.sqrt(xf * xf + _f(eps))
+            assert abs(y[0, 0] - want) <= 1e-15 * abs(want), (xv, eps)
+
+
+def pin_hand_n2(O):
+    """Hand-worked n = 2 rows (unit gain, eps = 1e-5 as f32)."""
+    e = _f(1e-5)
+    t = _f(1e-3)
+    cases = [
+        ([3.0, 4.0], [3 / math.sqrt(12.5 + e), 4 / math.sqrt(12.5 + e)]),
+        ([1.0, -1.0], [1 / math.sqrt(1 + e), -1 / math.sqrt(1 + e)]),
+        ([1.0, 0.0], [math.sqrt(2) / math.sqrt(1 + 2 * e), 0.0]),
+        ([t, t], [1 / math.sqrt(1 + e / (t * t))] * 2),
+        ([0.0, 0.0], [0.0, 0.0]),
+    ]
+    gamma = np.ones(2, F32)
+    for xs, want in cases:
+        y = O.rmsnorm(np.array([xs], F32), gamma, 1e-5)[0]
+        assert np.max(_rel(y, want)) < 2e-15, (xs, y, want)
+    # the epsilon-dominated [1e-3, 1e-3] row is far from unit scale: with
+    # decimal inputs it would be 1/sqrt(11); the f32 rounding of 1e-3 and 1e-5
+    # moves it by about 1.6e-8
+    y = O.rmsnorm(np.array([[t, t]], F32), gamma, 1e-5)[0]
+    assert abs(y[0] - 1 / math.sqrt(11)) < 3e-8
+
+
+def pin_tail_hand_example(O):
+    """a = [3, 4], r = [1, -1], unit gains, eps_post = 1e-8, eps_pre = 1e-5."""
+    ep, eq = _f(1e-8), _f(1e-5)
+    d_a = math.sqrt(12.5 + ep)
+    p = [3 / d_a, 4 / d_a]
+    h = [1 + p[0], -1 + p[1]]
+    d_h = math.sqrt((h[0] ** 2 + h[1] ** 2) / 2 + eq)
+    y = [h[0] / d_h, h[1] / d_h]
+    one = np.ones(2, F32)
+    t = O.sandwich_tail(np.array([[3, 4]], F32), np.array([[1, -1]], F32),
+                        one, 1e-8, one, 1e-5)
+    scale = np.abs([1.0, -1.0]) + np.abs(p)
+    assert np.max(_rel(t.p[0], p)) < 2e-15
+    assert np.all(np.abs(t.h[0] - h) <= 2e-15 * scale)
+    assert np.all(np.abs(t.y[0] - y) <= 4e-15 * scale / d_h)
+    assert abs(t.d_a[0] - d_a) < 1e-15 and abs(t.d_h[0] - d_h) < 1e-15
+    # worked through by hand to 12 digits
+    assert abs(t.h[0, 0] - 1.848528137084) < 1e-11
+    assert abs(t.h[0, 1] - 0.131370849446) < 1e-11
+    assert abs(t.y[0, 0] - 1.410651588865) < 1e-11
+    assert abs(t.y[0, 1] - 0.100251921398) < 1e-11
+
+
+def pin_eps_dominated(O):
+    """mean(x^2) = m << eps: y / (gamma x / sqrt(eps)) = (1 + m/eps)^(-1/2)
+    = 1 - m/(2 eps) + O((m/eps)^2)."""
+    rng = rng_for(13)
+    for eps in (1e-5, 1e-8, 1e-6):
+        for n in (2, 16, 300):
+            x = (rng.standard_normal((1, n)) * math.sqrt(eps) * 1e-3).astype(F32)
+            gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+            y = O.rmsnorm(x, gamma, eps)[0]
+            xd = x[0].astype(np.float64)
+            m = float(np.mean(xd * xd))
+            ratio = y / (gamma * xd / math.sqrt(_f(eps)))
+            t = m / _f(eps)
+            assert t < 1e-5
+            assert np.max(np.abs(ratio - (1 - t / 2))) <= t * t + 1e-15, eps
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def pin_unit_gain_mean_square(O):
+    """gamma = 1: mean(y^2) = m / (m + eps) with m = mean(x^2) (rms(y) = 1 in
+    the limit eps -> 0, the page's check after Figure 12.1)."""
+    rng = rng_for(14)
+    for n in (3, 64, 6656):
+        for lg in (-6, -2, 0, 3):
+            x = (rng.standard_normal((2, n)) * 10.0 ** lg).astype(F32)
+            y = O.rmsnorm(x, np.ones(n, F32), 1e-5)
+            xd = x.astype(np.float64)
+            m = np.mean(xd * xd, axis=1)
+            want = m / (m + _f(1e-5))
+            got = np.mean(y * y, axis=1)
+            assert np.max(_rel(got, want)) < 1e-13, (n, lg)
+
+
+def pin_scale_invariance(O):
+    """y(alpha x; eps) = y(x; eps / alpha^2) exactly for alpha a power of two
+    (every operation scales exactly), and y(alpha x) ~ y(x) when eps << m."""
+    rng = rng_for(15)
+    for n in (2, 5, 513):
+        x = (rng.standard_normal((3, n)) * 0.5).astype(F32)
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        eps = 2.0 ** -17
+        for k in (-20, -3, 5, 30):
+            alpha = 2.0 ** k
+            y1 = O.rmsnorm((x * F32(alpha)).astype(F32), gamma, eps)
+            y2 = O.rmsnorm(x, gamma, eps / alpha ** 2)
+            assert np.array_equal(y1, y2), (n, k)
+        # eps negligible: plain scale invariance up to ~eps/m
+        xd = x.astype(np.float64)
+        m = np.mean(xd * xd, axis=1, keepdims=True)
+        ya = O.rmsnorm((x * F32(1024.0)).astype(F32), gamma, 1e-8)
+        yb = O.rmsnorm(x, gamma, 1e-8)
+        assert np.all(np.abs(ya - yb) <= (1e-8 / m + 1e-15) * np.abs(yb) + 1e-15)
+
+
+def pin_row_independence(O):
+    """A batch of rows equals each row normalised on its own (row stride n)."""
+    rng = rng_for(16)
+    for n in (1, 3, 8, 77):
+        x = rng.standard_normal((5, n)).astype(F32)
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        yb = O.rmsnorm(x, gamma, 1e-5)
+        for i in range(5):
+            assert np.array_equal(yb[i], O.rmsnorm(x[i:i + 1], gamma, 1e-5)[0])
+        a = rng.standard_normal((4, n)).astype(F32)
+        r = rng.standard_normal((4, n)).astype(F32)
+        tb = O.sandwich_tail(a, r, gamma, 1e-8, gamma[::-1].copy(), 1e-5)
+        for i in range(4):
+            ti = O.sandwich_tail(a[i:i + 1], r[i:i + 1], gamma, 1e-8,
+                                 gamma[::-1].copy(), 1e-5)
+            assert np.array_equal(tb.h[i], ti.h[0])
+            assert np.array_equal(tb.y[i], ti.y[0])
+
+
+# ---------------------------------------------------------------------------
+# Library routines
+# ---------------------------------------------------------------------------
+
+def pin_torch_rms_norm(O):
+    import torch
+    import torch.nn.functional as F
+    rng = rng_for(17)
+    for n, lg in ((4, 0), (128, -3), (6656, 1), (6657, -5), (2, 2)):
+        x = (rng.standard_normal((6, n)) * 10.0 ** lg).astype(F32)
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        for eps in (1e-5, 1e-8):
+            want = F.rms_norm(torch.from_numpy(x).double(), (n,),
+                              torch.from_numpy(gamma).double(),
+                              eps=_f(eps)).numpy()
+            got = O.rmsnorm(x, gamma, eps)
+            assert np.max(_rel(got, want)) < 1e-13, (n, eps)
+
+
+def pin_layer_norm_identity(O):
+    """On rows whose mean is exactly zero, LayerNorm without bias equals
+    RMSNorm. Rows are symmetric multisets of multiples of 1/16, so every sum is
+    exact in f64 whatever order a library adds in."""
+    import torch
+    import torch.nn.functional as F
+    rng = rng_for(18)
+    for half in (1, 3, 50, 2000):
+        k = rng.integers(-100, 101, half)
+        vals = np.concatenate([k, -k]) / 16.0
+        x = rng.permutation(vals).astype(F32)[None, :]
+        n = x.shape[1]
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        for eps in (1e-5, 1e-8):
+            want = F.layer_norm(torch.from_numpy(x).double(), (n,),
+                                torch.from_numpy(gamma).double(), None,
+                                eps=_f(eps)).numpy()
+            got = O.rmsnorm(x, gamma, eps)
+            assert np.max(_rel(got, want)) < 1e-13, (n, eps)
+
+
+# ---------------------------------------------------------------------------
+# Exact arithmetic on tiny inputs
+# ---------------------------------------------------------------------------
+
+def _dec_rms(xs, gs, eps):
+    n = len(xs)
+    s = sum((x * x for x in xs), Decimal(0))
+    rms = (s / Decimal(n) + eps).sqrt()
+    return [x / rms * g for x, g in zip(xs, gs)], rms
+
+
+def _tiny_rows(rng, count, nmax):
+    rows = []
+    for i in range(count):
+        n = int(rng.integers(1, nmax + 1))
+        lg = rng.uniform(-5, 3)
+        rows.append((rng.standard_normal(n) * 10.0 ** lg).astype(F32))
+    return rows
+
+
+def pin_decimal_plain(O):
+    getcontext().prec = 50
+    rng = rng_for(19)
+    for x in _tiny_rows(rng, 60, 16):
+        n = x.size
+        gamma = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        for eps in (1e-5, 1e-8):
+            want, _ = _dec_rms([Decimal(float(v)) for v in x],
+                               [Decimal(float(v)) for v in gamma],
+                               Decimal(_f(eps)))
+            got = O.rmsnorm(x[None, :], gamma, eps)[0]
+            want = np.array([float(w) for w in want])
+            assert np.max(_rel(got, want)) < 1e-14, (n, eps)
+
+
+def pin_decimal_bf16(O):
+    """bf16 storage is decoded exactly: the bf16 result equals the exact value
+    on the decoded inputs, and equals the f32 path on the same values."""
+    getcontext().prec = 50
+    rng = rng_for(20)
+    for x in _tiny_rows(rng, 40, 16):
+        n = x.size
+        xb = f32_to_bf16_bits(x)
+        gb = f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(n)).astype(F32))
+        xd, gd = bf16_bits_to_f32(xb), bf16_bits_to_f32(gb)
+        want, _ = _dec_rms([Decimal(float(v)) for v in xd],
+                           [Decimal(float(v)) for v in gd], Decimal(_f(1e-6)))
+        got = O.rmsnorm(xb[None, :], gb, 1e-6)[0]
+        want = np.array([float(w) for w in want])
+        assert np.max(_rel(got, want)) < 1e-14
+        assert np.array_equal(got, O.rmsnorm(xd[None, :], gd, 1e-6)[0])
+
+
+def pin_decimal_tail(O):
+    """Exact fused tail. Rows are drawn so that mean(a^2) sits near eps_post
+    and mean(h^2) near eps_pre in some rows: swapping or dropping either
+    epsilon changes those rows by far more than the tolerance."""
+    getcontext().prec = 50
+    rng = rng_for(21)
+    ep, eq = Decimal(_f(1e-8)), Decimal(_f(1e-5))
+    for i in range(60):
+        n = int(rng.integers(1, 17))
+        a_lg = rng.choice([-4.0, -4.5, -2.0, 0.0, 1.5])
+        r_lg = rng.choice([-3.0, -2.5, -1.0, 0.5])
+        a = (rng.standard_normal(n) * 10.0 ** a_lg).astype(F32)
+        r = (rng.standard_normal(n) * 10.0 ** r_lg).astype(F32)
+        gp = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        gq = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        ad = [Decimal(float(v)) for v in a]
+        p, d_a = _dec_rms(ad, [Decimal(float(v)) for v in gp], ep)
+        h = [Decimal(float(rv)) + pv for rv, pv in zip(r, p)]
+        y, d_h = _dec_rms(h, [Decimal(float(v)) for v in gq], eq)
+        t = O.sandwich_tail(a[None, :], r[None, :], gp, 1e-8, gq, 1e-5)
+        scale = np.abs(r.astype(np.float64)) + np.abs([float(v) for v in p])
+        hw = np.array([float(v) for v in h])
+        yw = np.array([float(v) for v in y])
+        assert np.all(np.abs(t.h[0] - hw) <= 1e-14 * scale + 1e-300), i
+        yscale = np.abs(gq.astype(np.float64)) * scale / float(d_h)
+        assert np.all(np.abs(t.y[0] - yw) <= 1e-14 * yscale + 1e-300), i
+        assert abs(t.d_a[0] - float(d_a)) <= 1e-14 * float(d_a)
+        assert abs(t.d_h[0] - float(d_h)) <= 1e-14 * float(d_h)
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_constant_rows,
+    pin_zero_rows,
+    pin_n1,
+    pin_hand_n2,
+    pin_tail_hand_example,
+    pin_eps_dominated,
+    pin_unit_gain_mean_square,
+    pin_scale_invariance,
+    pin_row_independence,
+    pin_torch_rms_norm,
+    pin_layer_norm_identity,
+    pin_decimal_plain,
+    pin_decimal_bf16,
+    pin_decimal_tail,
+]
