@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+Default workload: the fused dual-epsilon sandwich tail on 4096 rows x 6656
+f32 (reads a and r, writes h and y: four row streams), with the gains and
+epsilons of the model the Muser book describes (eps_post = 1e-8,
+eps_pre = 1e-5). A step is one sandwich_tail call over the whole batch.
+
+Prints ONE JSON line on stdout: achieved HBM GB/s from algorithmic bytes
+(row streams plus each gain once per launch) over wall time, rows/s, the
+dominant kernel's roofline (per-launch time from HIP events on the launch
+stream) and the f64 oracle's throughput on the host cores.
+
+Inputs are resident in HBM before timing starts. Three (default) rotating
+sets of input/output buffers, together larger than twice the 256 MB
+Infinity Cache, keep one launch's inputs from being served by the cache the
+previous launch warmed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("achieved HBM GB/s (% of peak) + rows/s, fused sandwich tail "
+          "4096×6656 f32")
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg) -> int:
+    es = 2 if cfg.dtype == "bf16" else 4
+    streams = 4 if cfg.kind == "tail" else 2
+    gains = 2 if cfg.kind == "tail" else 1
+    return streams * cfg.rows * cfg.n * es + gains * cfg.n * es
+
+
+def make_device_sets(cfg, inp, sets, torch):
+    dev = torch.device("cuda:0")
+    out = []
+    if cfg.kind == "tail":
+        base = {k: torch.from_numpy(inp[k]).to(dev)
+                for k in ("a", "r", "gamma_post", "gamma_pre")}
+        for _ in range(sets):
+            out.append({"a": base["a"].clone(), "r": base["r"].clone(),
+                        "gp": base["gamma_post"], "gq": base["gamma_pre"],
+                        "h": torch.empty_like(base["a"]),
+                        "y": torch.empty_like(base["a"])})
+    else:
+        import numpy as np
+        if cfg.dtype == "bf16":
+            x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(
+                torch.bfloat16)
+            g = torch.from_numpy(inp["gamma"].view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        else:
+            x = torch.from_numpy(inp["x"]).to(dev)
+            g = torch.from_numpy(inp["gamma"]).to(dev)
+        for _ in range(sets):
+            out.append({"x": x.clone(), "g": g, "y": torch.empty_like(x)})
+    return out
+
+
+def cpu_baseline(cfg, inp, seconds: float) -> dict:
+    """The f64 oracle as it stands, rows split across host threads (ctypes
+    releases the GIL), repeated over the full workload for about `seconds`."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    O = oracle.load()
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    rows = cfg.rows
+    bounds = [(rows * i // cores, rows * (i + 1) // cores)
+              for i in range(cores)]
+    bounds = [b for b in bounds if b[1] > b[0]]
+
+    def one(b):
+        lo, hi = b
+        if cfg.kind == "tail":
+            O.sandwich_tail(inp["a"][lo:hi], inp["r"][lo:hi],
+                            inp["gamma_post"], inp["eps_post"],
+                            inp["gamma_pre"], inp["eps_pre"])
+        else:
+            O.rmsnorm(inp["x"][lo:hi], inp["gamma"], inp["eps"])
+
+    passes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(len(bounds)) as ex:
+        while True:
+            list(ex.map(one, bounds))
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    gbs = algorithmic_bytes(cfg) * passes / dt / 1e9
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": len(bounds),
+            "kind": "oracle",
+            "sample": (f"{passes} full passes over {cfg.name} "
+                       f"({rows} rows) in {dt:.1f} s, scalar f64 C oracle, "
+                       f"rows split over {len(bounds)} threads; "
+                       f"rows/s {rows * passes / dt:.4g}; cpu: {model}")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=None,
+                    help="workload name (default: the 4096x6656 f32 tail)")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="rotating buffer sets (defeat the Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run 10 plain device copies of MIB MiB "
+                         "(byte-counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (rows shard across GPUs with no communication; see the "
+              "design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sandwich_norm_residual_amd as snr
+    from sandwich_norm_residual_amd import _lib
+    from sandwich_norm_residual_amd import inputs as gen
+    if not os.path.exists(_lib.LIBRARY):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    cfg = gen.CONFIGS[args.config or gen.HEADLINE]
+    log(f"workload {cfg.name}: rows={cfg.rows} n={cfg.n} {cfg.dtype} "
+        f"seed={cfg.seed}")
+    inp = gen.make(cfg)
+    sets = make_device_sets(cfg, inp, args.sets, torch)
+    stream = torch.cuda.Stream()   # default priority
+    nbytes = algorithmic_bytes(cfg)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        if cfg.kind == "tail":
+            snr.sandwich_tail(s["a"], s["r"], s["gp"], inp["eps_post"],
+                              s["gq"], inp["eps_pre"], h_out=s["h"],
+                              y_out=s["y"])
+        else:
+            snr.rmsnorm_fwd(s["x"], s["g"], inp["eps"], out=s["y"])
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        shape = snr.last_shape()
+        torch.cuda.synchronize()
+
+        # whole-job throughput: K back-to-back steps, synchronised both sides
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+        # per-launch kernel time with events on the launch stream
+        ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        durs_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+        if args.copy_probe:
+            n = args.copy_probe * (1 << 20) // 4
+            src = torch.ones(n, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(10):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"copy probe: 10 x {args.copy_probe} MiB device copies")
+
+    ms_per_step = wall / args.steps * 1e3
+    value = nbytes * args.steps / wall / 1e9
+    mean_us = statistics.fmean(durs_us)
+    med_us = statistics.median(durs_us)
+    q = statistics.quantiles(durs_us, n=10)
+    achieved = nbytes / (mean_us * 1e-6) / 1e9
+    log(f"shape {shape}; wall {ms_per_step * 1e3:.2f} us/step; events mean "
+        f"{mean_us:.2f} us median {med_us:.2f} p10 {q[0]:.2f} p90 {q[-1]:.2f}")
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC if cfg.name == gen.HEADLINE else
+        f"achieved HBM GB/s + rows/s, {cfg.name}",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": (f"synthetic: seeded PCG64 (seed {cfg.seed}) Gaussian rows "
+                 "with log-uniform per-row scales, gains 1+0.1*N(0,1)"),
+        "config": {"workload": cfg.name, "rows": cfg.rows, "n": cfg.n,
+                   "kind": cfg.kind, "eps": list(cfg.eps),
+                   "dispatch_shape": shape,
+                   "rotating_buffer_sets": len(sets),
+                   "algorithmic_bytes_per_step": nbytes},
+        "rows_per_s": round(cfg.rows * args.steps / wall, 1),
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "kernel_us": {"mean": round(mean_us, 3), "median": round(med_us, 3),
+                      "p10": round(q[0], 3), "p90": round(q[-1], 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

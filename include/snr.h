@@ -1,0 +1,173 @@
+/*
+ * snr.h - C ABI of libsnr: row-wise RMSNorm and the fused dual-epsilon
+ * sandwich tail on AMD Instinct MI355X (gfx950), hand-written HIP kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, contiguous, row-major [rows, n] arrays in device
+ *   memory (row i starts at element i*n); gains are dense [n] vectors shared
+ *   by all rows. There is no stride argument.
+ * - All pointers are device pointers owned by the caller. The library never
+ *   frees or retains them. It owns only a small per-(device, stream) workspace
+ *   that the split-row kernels use for cross-workgroup partial sums; it is
+ *   allocated on first need and released at process exit.
+ * - Calls are asynchronous: they validate the arguments, enqueue kernels on
+ *   `stream` (NULL = the legacy default stream of the current device) and
+ *   return. Execution faults surface at the caller's next synchronisation.
+ *   Arguments are never partially processed: a call that returns an error
+ *   code has enqueued nothing.
+ * - Reductions are deterministic: for a given (rows, n, dtype, dispatch
+ *   shape) the result is bit-identical from run to run (fixed summation
+ *   order, no floating-point atomics).
+ * - Every n >= 1 is computed; there is no refusal by row width. rows == 0 is
+ *   a successful no-op. n is limited to 2^31 - 1 elements per row.
+ * - Return value: SNR_OK (0) or one of the SNR_ERR_* codes below.
+ */
+#ifndef SNR_H
+#define SNR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SNR_API __attribute__((visibility("default")))
+#else
+#define SNR_API
+#endif
+
+/* An opaque HIP stream handle (identical to HIP's own hipStream_t). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    SNR_F32 = 0,  /* IEEE binary32 storage */
+    SNR_BF16 = 1  /* bfloat16 storage; arithmetic in f32, output rounded to
+                     nearest-even */
+} snr_dtype;
+
+enum {
+    SNR_OK = 0,
+    SNR_ERR_NULL = 1,      /* a required pointer is NULL while rows > 0 */
+    SNR_ERR_SHAPE = 2,     /* n < 1, n > 2^31 - 1, rows < 0, or rows*n
+                              overflows */
+    SNR_ERR_DTYPE = 3,     /* dtype is not an snr_dtype value */
+    SNR_ERR_EPS = 4,       /* an epsilon is not finite or not > 0 */
+    SNR_ERR_ALIAS = 5,     /* buffers overlap other than in an allowed way */
+    SNR_ERR_ALIGN = 6,     /* a pointer is not aligned to its element size */
+    SNR_ERR_WORKSPACE = 7, /* the split-row workspace could not be set up,
+                              or the row is too wide for co-resident
+                              workgroups */
+    SNR_ERR_HIP = 8,       /* a HIP runtime call failed; see
+                              snr_last_hip_error() */
+    SNR_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+};
+
+/*
+ * rmsnorm_fwd - row-wise RMSNorm.
+ *
+ * Defined in "RMSNorm and the dual-epsilon sandwich" (Muser book, chapter
+ * 12), section 12.1 "What it computes": for each row i
+ *     y[i, j] = x[i, j] / sqrt( (1/n) * sum_k x[i, k]^2 + eps ) * gamma[j]
+ * with epsilon inside the root (the same three steps Hesper's RMSNorm layer
+ * documents for rmsNormKernel).
+ *
+ *   x      [rows, n] input, dtype `dtype`, device memory
+ *   gamma  [n] per-channel gain, same dtype as x
+ *   eps    epsilon added to the mean of squares; finite and > 0
+ *   rows   number of rows (>= 0)
+ *   n      row width (>= 1)
+ *   dtype  SNR_F32 or SNR_BF16 (storage of x, gamma and y). Accumulation and
+ *          arithmetic are f32 in both cases; bf16 output is rounded to
+ *          nearest-even.
+ *   y      [rows, n] output, dtype `dtype`. y == x (exactly the same
+ *          pointer) is allowed and computes in place; any other overlap of y
+ *          with x or gamma is SNR_ERR_ALIAS.
+ *   stream HIP stream to enqueue on (NULL = default stream)
+ *
+ * Pointers need only element alignment (4 B for f32, 2 B for bf16); 16-byte
+ * aligned rows (and n a multiple of 4 for f32, 8 for bf16) select 128-bit
+ * loads, anything else selects element-wide loads.
+ */
+SNR_API int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
+                int64_t n, int dtype, void *y, hipStream_t stream);
+
+/*
+ * sandwich_tail - the fused dual-epsilon sandwich tail, f32 storage.
+ *
+ * Defined in "RMSNorm and the dual-epsilon sandwich" (Muser book, chapter
+ * 12): section 12.2 gives the layer order (a sub-block's output is
+ * post-normed before it is added to the residual stream, and the stream is
+ * pre-normed before the next sub-block reads it) and section 12.4.3 the fused
+ * tail that performs post-norm, residual add and the next pre-norm in one
+ * dispatch with two different epsilons. Per row:
+ *     h = r + gamma_post * a / sqrt(mean(a^2) + eps_post)
+ *     y = gamma_pre * h / sqrt(mean(h^2) + eps_pre)
+ * The model the book describes uses eps_post = 1e-8 and eps_pre = 1e-5; both
+ * are arguments here. y is computed from the f32 value of h that is stored.
+ * Hesper's residualAddRmsNormKernel ("Hesper.Layers.RMSNorm") writes both the
+ * updated stream and its norm the same way.
+ *
+ *   a          [rows, n] sub-block output (e.g. the attention or FFN result)
+ *   r          [rows, n] residual stream before the add
+ *   gamma_post [n] post-norm gain;  eps_post its epsilon (finite, > 0)
+ *   gamma_pre  [n] pre-norm gain;   eps_pre its epsilon (finite, > 0)
+ *   h_out      [rows, n] updated residual stream. h_out == r (exactly) is
+ *              allowed and updates the stream in place.
+ *   y_out      [rows, n] normalised input of the next sub-block
+ *   rows, n    as for rmsnorm_fwd
+ *   stream     HIP stream (NULL = default stream)
+ *
+ * SNR_ERR_ALIAS: y_out overlapping any other buffer, h_out overlapping a or
+ * a gain, or h_out partially overlapping r.
+ */
+SNR_API int sandwich_tail(const float *a, const float *r, const float *gamma_post,
+                  float eps_post, const float *gamma_pre, float eps_pre,
+                  float *h_out, float *y_out, int64_t rows, int64_t n,
+                  hipStream_t stream);
+
+/* Human-readable text for an SNR_* code (static storage, never NULL). */
+SNR_API const char *snr_strerror(int code);
+
+/* The hipError_t of the most recent failing HIP call made by this library on
+ * the calling thread (0 if none since the last successful call). */
+SNR_API int snr_last_hip_error(void);
+
+/*
+ * Dispatch-shape introspection and override (diagnostics and tests).
+ *
+ * Shapes:  SNR_SHAPE_AUTO     choose by n, rows, dtype and alignment
+ *          SNR_SHAPE_ROWTILE  g lanes per row (g a power of two, 1..1024),
+ *                             each lane holding `vpt` loads of the row in
+ *                             registers; g <= 64 packs several rows in one
+ *                             wavefront, g > 64 spans g/64 wavefronts joined
+ *                             by one LDS step
+ *          SNR_SHAPE_SPLIT    the row is cut into chunks of 256 x `vpt`
+ *                             loads, one workgroup per chunk, joined by a
+ *                             two-phase cross-workgroup reduction
+ * snr_force_shape applies to subsequent calls on the calling thread until it
+ * is called again with SNR_SHAPE_AUTO. A forced shape that cannot hold the
+ * row (g * vpt loads < row length) or that has no compiled kernel returns
+ * SNR_ERR_SHAPE from the call. snr_last_shape writes "kind:g:vpt:width" of the
+ * calling thread's most recent successful launch into buf (NUL-terminated).
+ */
+enum { SNR_SHAPE_AUTO = 0, SNR_SHAPE_ROWTILE = 1, SNR_SHAPE_SPLIT = 2 };
+SNR_API int snr_force_shape(int kind, int g, int vpt);
+SNR_API int snr_last_shape(char *buf, int len);
+
+/*
+ * Split-row wait watchdog. The split-row kernels wait for the partial sums
+ * of the other workgroups of their row with a bounded spin; if the bound is
+ * ever exceeded the kernel stops waiting, records the event in the stream's
+ * workspace and finishes (its outputs are then invalid). This returns the
+ * number of such events recorded on (current device, stream) and clears the
+ * count. It synchronises the stream. 0 means every wait completed normally.
+ */
+SNR_API int snr_split_timeouts(hipStream_t stream, int64_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNR_H */

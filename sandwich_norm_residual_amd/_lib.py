@@ -1,0 +1,115 @@
+"""ctypes view of libsnr.so (the C ABI declared in include/snr.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind these symbols. If the library has not been built this module
+raises; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libsnr.so")
+
+SNR_F32 = 0
+SNR_BF16 = 1
+
+SNR_OK = 0
+SNR_ERR_NULL = 1
+SNR_ERR_SHAPE = 2
+SNR_ERR_DTYPE = 3
+SNR_ERR_EPS = 4
+SNR_ERR_ALIAS = 5
+SNR_ERR_ALIGN = 6
+SNR_ERR_WORKSPACE = 7
+SNR_ERR_HIP = 8
+SNR_ERR_DEVICE = 9
+
+SHAPE_AUTO = 0
+SHAPE_ROWTILE = 1
+SHAPE_SPLIT = 2
+
+# Every function include/snr.h declares, with its ctypes signature.
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+_int = ctypes.c_int
+SIGNATURES = {
+    "rmsnorm_fwd": (_int, [_vp, _vp, _f, _i64, _i64, _int, _vp, _vp]),
+    "sandwich_tail": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp, _i64,
+                             _i64, _vp]),
+    "snr_strerror": (ctypes.c_char_p, [_int]),
+    "snr_last_hip_error": (_int, []),
+    "snr_force_shape": (_int, [_int, _int, _int]),
+    "snr_last_shape": (_int, [ctypes.c_char_p, _int]),
+    "snr_split_timeouts": (_int, [_vp, ctypes.POINTER(_i64)]),
+}
+
+_LIB = None
+
+
+class SnrError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        text = strerror(code)
+        if code == SNR_ERR_HIP:
+            text += f" (hipError_t {lib().snr_last_hip_error()})"
+        super().__init__(f"{where}: {text} [code {code}]")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsnr.so once; raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is not built; run "
+                "`python -m sandwich_norm_residual_amd.build` first")
+        handle = ctypes.CDLL(LIBRARY)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def strerror(code: int) -> str:
+    return lib().snr_strerror(code).decode()
+
+
+def check(code: int, where: str) -> None:
+    if code != SNR_OK:
+        raise SnrError(code, where)
+
+
+def rmsnorm_fwd(x: int, gamma: int, eps: float, rows: int, n: int,
+                dtype: int, y: int, stream: int) -> int:
+    """Raw call with integer device addresses; returns the SNR_* code."""
+    return lib().rmsnorm_fwd(x, gamma, eps, rows, n, dtype, y, stream)
+
+
+def sandwich_tail(a: int, r: int, gamma_post: int, eps_post: float,
+                  gamma_pre: int, eps_pre: float, h_out: int, y_out: int,
+                  rows: int, n: int, stream: int) -> int:
+    """Raw call with integer device addresses; returns the SNR_* code."""
+    return lib().sandwich_tail(a, r, gamma_post, eps_post, gamma_pre, eps_pre,
+                               h_out, y_out, rows, n, stream)
+
+
+def force_shape(kind: int, g: int = 0, vpt: int = 0) -> None:
+    check(lib().snr_force_shape(kind, g, vpt), "snr_force_shape")
+
+
+def last_shape() -> str:
+    buf = ctypes.create_string_buffer(64)
+    check(lib().snr_last_shape(buf, 64), "snr_last_shape")
+    return buf.value.decode()
+
+
+def split_timeouts(stream: int) -> int:
+    out = _i64(0)
+    check(lib().snr_split_timeouts(stream, ctypes.byref(out)),
+          "snr_split_timeouts")
+    return out.value

@@ -1,0 +1,435 @@
+// snr_api.cpp - the C ABI of libsnr (declared in include/snr.h): argument
+// validation, dispatch-shape selection, the split-row workspace and the
+// kernel launches. Host code only; the kernels live in snr_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "snr.h"
+#include "snr_internal.h"
+
+namespace snr {
+namespace {
+
+thread_local int t_last_hip_error = 0;
+thread_local int t_force_kind = SNR_SHAPE_AUTO;
+thread_local int t_force_g = 0;
+thread_local int t_force_vpt = 0;
+thread_local char t_last_shape[64] = "";
+
+int hip_fail(hipError_t e) {
+    t_last_hip_error = (int)e;
+    return SNR_ERR_HIP;
+}
+
+bool debug_enabled() {
+    static const bool on = [] {
+        const char *v = std::getenv("SNR_DEBUG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// ---------------------------------------------------------------------------
+// Device facts (cached per device ordinal)
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+    bool ok = false;   // gfx950
+    int cus = 0;
+};
+
+std::mutex g_dev_mu;
+std::map<int, DeviceInfo> g_dev;
+
+int current_device(int *dev, DeviceInfo *info) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_dev.find(*dev);
+    if (it == g_dev.end()) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, *dev);
+        if (e != hipSuccess) return hip_fail(e);
+        DeviceInfo d;
+        d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        it = g_dev.emplace(*dev, d).first;
+    }
+    *info = it->second;
+    return info->ok ? SNR_OK : SNR_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// Split-row workspace, one per (device, stream)
+// ---------------------------------------------------------------------------
+constexpr int64_t kSlotCap = int64_t(1) << 18;  // partial slots per set
+constexpr int64_t kRowCap = int64_t(1) << 18;   // rows per launch
+constexpr uint32_t kSpinLimit = 1u << 22;       // polls before giving up
+
+struct Workspace {
+    void *base = nullptr;
+    int64_t words = 0;
+    SplitState st{};
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(int dev, hipStream_t stream, SplitState *out) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto key = std::make_pair(dev, stream);
+    auto it = g_ws.find(key);
+    if (it == g_ws.end()) {
+        Workspace w;
+        const int64_t slot_bytes = 2 * kSlotCap * 8;
+        const int64_t depart_bytes = 2 * kRowCap * 4;
+        const int64_t bytes = slot_bytes + depart_bytes + 256;
+        hipError_t e = hipMalloc(&w.base, (size_t)bytes);
+        if (e != hipSuccess) {
+            t_last_hip_error = (int)e;
+            return SNR_ERR_WORKSPACE;
+        }
+        w.words = bytes / 4;
+        e = zero_words(w.base, w.words, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(w.base);
+            return hip_fail(e);
+        }
+        char *b = static_cast<char *>(w.base);
+        w.st.slots = reinterpret_cast<unsigned long long *>(b);
+        w.st.depart = reinterpret_cast<unsigned int *>(b + slot_bytes);
+        w.st.ticket =
+            reinterpret_cast<unsigned int *>(b + slot_bytes + depart_bytes);
+        w.st.timeouts = w.st.ticket + 16;
+        w.st.slot_cap = kSlotCap;
+        w.st.row_cap = kRowCap;
+        w.st.spin_limit = kSpinLimit;
+        it = g_ws.emplace(key, w).first;
+    }
+    *out = it->second.st;
+    return SNR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb) {
+    if (!p || !q || pb <= 0 || qb <= 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)qb && b < a + (uintptr_t)pb;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool eps_ok(float e) { return std::isfinite(e) && e > 0.0f; }
+
+int check_shape(int64_t rows, int64_t n, int64_t esize) {
+    if (rows < 0 || n < 1 || n > INT32_MAX) return SNR_ERR_SHAPE;
+    if (rows > 0 && rows > (INT64_MAX / esize) / n) return SNR_ERR_SHAPE;
+    return SNR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Shape selection
+// ---------------------------------------------------------------------------
+struct Choice {
+    const KernelEntry *k = nullptr;
+    int chunks = 0;  // split only
+};
+
+const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
+                              int vpt) {
+    int count = 0;
+    const KernelEntry *t = kernel_table(&count);
+    for (int i = 0; i < count; ++i)
+        if (t[i].op == op && t[i].storage == st && t[i].width == w &&
+            t[i].kind == kind && (kind == KIND_SPLIT || t[i].g == g) &&
+            t[i].vpt == vpt)
+            return &t[i];
+    return nullptr;
+}
+
+constexpr int64_t kSplitAbove = 8192;  // loads per row above which rows split
+
+int split_chunks(const KernelEntry *k, int64_t nv) {
+    const int64_t per = (int64_t)kSplitBlock * k->vpt;
+    return (int)((nv + per - 1) / per);
+}
+
+int choose(int op, int st, int w, int64_t nv, int64_t rows,
+           const DeviceInfo &dev, Choice *c) {
+    if (t_force_kind == SNR_SHAPE_ROWTILE) {
+        c->k = find_entry(op, st, w, KIND_ROWTILE, t_force_g, t_force_vpt);
+        if (!c->k || (int64_t)c->k->g * c->k->vpt < nv) return SNR_ERR_SHAPE;
+        return SNR_OK;
+    }
+    if (t_force_kind == SNR_SHAPE_SPLIT) {
+        c->k = find_entry(op, st, w, KIND_SPLIT, 0, t_force_vpt);
+        if (!c->k) return SNR_ERR_SHAPE;
+        c->chunks = split_chunks(c->k, nv);
+        return SNR_OK;
+    }
+    if (nv > kSplitAbove) {
+        c->k = find_entry(op, st, w, KIND_SPLIT, 0, 8);
+        if (!c->k) return SNR_ERR_SHAPE;
+        c->chunks = split_chunks(c->k, nv);
+        return SNR_OK;
+    }
+    if (nv <= 128) {
+        int g = 1;
+        while (g * 4 < nv) g *= 2;
+        c->k = find_entry(op, st, w, KIND_ROWTILE, g, 4);
+        return c->k ? SNR_OK : SNR_ERR_SHAPE;
+    }
+    if (nv <= 1024) {
+        int vpt = 2;
+        while (64 * vpt < nv) vpt *= 2;
+        c->k = find_entry(op, st, w, KIND_ROWTILE, 64, vpt);
+        return c->k ? SNR_OK : SNR_ERR_SHAPE;
+    }
+    // One workgroup per row: the smallest register tile that holds the row;
+    // among equal tiles the widest workgroup. When the rows alone cannot
+    // fill the chip (fewer than 4 wavefronts per CU), use the widest
+    // workgroup that holds the row so each row is fetched by more lanes.
+    int count = 0;
+    const KernelEntry *t = kernel_table(&count);
+    const KernelEntry *best = nullptr;
+    for (int i = 0; i < count; ++i) {
+        const KernelEntry &e = t[i];
+        if (e.op != op || e.storage != st || e.width != w ||
+            e.kind != KIND_ROWTILE || e.g < 128)
+            continue;
+        const int64_t cap = (int64_t)e.g * e.vpt;
+        if (cap < nv) continue;
+        if (!best) { best = &e; continue; }
+        const int64_t bcap = (int64_t)best->g * best->vpt;
+        if (cap < bcap || (cap == bcap && e.g > best->g)) best = &e;
+    }
+    if (!best) return SNR_ERR_SHAPE;
+    const int64_t waves = rows * (best->g / 64);
+    if (waves < 4LL * dev.cus) {
+        const KernelEntry *wide = nullptr;
+        for (int i = 0; i < count; ++i) {
+            const KernelEntry &e = t[i];
+            if (e.op != op || e.storage != st || e.width != w ||
+                e.kind != KIND_ROWTILE || e.g != 1024)
+                continue;
+            if ((int64_t)e.g * e.vpt < nv) continue;
+            if (!wide || e.vpt < wide->vpt) wide = &e;
+        }
+        if (wide) best = wide;
+    }
+    c->k = best;
+    return SNR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+int launch(int op, int st, int64_t esize, const RowArgs &args_in,
+           bool vec_ok, hipStream_t stream) {
+    int dev = 0;
+    DeviceInfo info;
+    int rc = current_device(&dev, &info);
+    if (rc != SNR_OK) return rc;
+
+    const int w = vec_ok ? (int)(16 / esize) : 1;
+    RowArgs a = args_in;
+    a.nv = (int32_t)(a.n / w);
+    Choice c;
+    rc = choose(op, st, w, a.nv, a.rows, info, &c);
+    if (rc != SNR_OK) return rc;
+    const KernelEntry *k = c.k;
+
+    if (k->kind == KIND_ROWTILE) {
+        const int rpb = k->block / k->g;
+        const int64_t max_blocks = (int64_t)(UINT32_MAX / (uint32_t)k->block);
+        const int64_t step = max_blocks * rpb;
+        for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
+            const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
+            hipError_t e = k->rowtile(a, r0, nr, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    } else {
+        if (c.chunks > kSplitMaxChunks) return SNR_ERR_SHAPE;
+        int per_cu = 0;
+        hipError_t e = k->occupancy(&per_cu);
+        if (e != hipSuccess) return hip_fail(e);
+        if ((int64_t)per_cu * info.cus < c.chunks) return SNR_ERR_WORKSPACE;
+        SplitState ws;
+        rc = get_workspace(dev, stream, &ws);
+        if (rc != SNR_OK) return rc;
+        int64_t step = kSlotCap / c.chunks;
+        if (step > kRowCap) step = kRowCap;
+        for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
+            const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
+            e = k->split(a, ws, r0, nr, c.chunks, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    }
+    if (k->kind == KIND_ROWTILE)
+        std::snprintf(t_last_shape, sizeof t_last_shape, "rowtile:%d:%d:%d",
+                      k->g, k->vpt, w);
+    else
+        std::snprintf(t_last_shape, sizeof t_last_shape, "split:%d:%d:%d:%d",
+                      k->g, k->vpt, w, c.chunks);
+    if (debug_enabled())
+        std::fprintf(stderr, "[snr] %s rows=%lld n=%d -> %s\n",
+                     op == OP_TAIL ? "sandwich_tail" : "rmsnorm_fwd",
+                     (long long)a.rows, a.n, t_last_shape);
+    t_last_hip_error = 0;
+    return SNR_OK;
+}
+
+}  // namespace
+}  // namespace snr
+
+using namespace snr;
+
+extern "C" {
+
+int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
+                int64_t n, int dtype, void *y, hipStream_t stream) {
+    if (dtype != SNR_F32 && dtype != SNR_BF16) return SNR_ERR_DTYPE;
+    const int64_t es = dtype == SNR_F32 ? 4 : 2;
+    int rc = check_shape(rows, n, es);
+    if (rc != SNR_OK) return rc;
+    if (!eps_ok(eps)) return SNR_ERR_EPS;
+    if (rows == 0) return SNR_OK;
+    if (!x || !gamma || !y) return SNR_ERR_NULL;
+    if (!aligned(x, es) || !aligned(gamma, es) || !aligned(y, es))
+        return SNR_ERR_ALIGN;
+    const int64_t tb = rows * n * es, gb = n * es;
+    if (y != x && overlaps(y, tb, x, tb)) return SNR_ERR_ALIAS;
+    if (overlaps(y, tb, gamma, gb)) return SNR_ERR_ALIAS;
+
+    const int w = (int)(16 / es);
+    const bool vec = n % w == 0 && aligned(x, 16) && aligned(y, 16) &&
+                     aligned(gamma, 16);
+    RowArgs a{};
+    a.x0 = x;
+    a.g0 = gamma;
+    a.out0 = y;
+    a.eps0 = eps;
+    a.rows = rows;
+    a.n = (int32_t)n;
+    return launch(OP_PLAIN, dtype == SNR_F32 ? ST_F32 : ST_BF16, es, a, vec,
+                  stream);
+}
+
+int sandwich_tail(const float *a, const float *r, const float *gamma_post,
+                  float eps_post, const float *gamma_pre, float eps_pre,
+                  float *h_out, float *y_out, int64_t rows, int64_t n,
+                  hipStream_t stream) {
+    int rc = check_shape(rows, n, 4);
+    if (rc != SNR_OK) return rc;
+    if (!eps_ok(eps_post) || !eps_ok(eps_pre)) return SNR_ERR_EPS;
+    if (rows == 0) return SNR_OK;
+    if (!a || !r || !gamma_post || !gamma_pre || !h_out || !y_out)
+        return SNR_ERR_NULL;
+    const void *ptrs[] = {a, r, gamma_post, gamma_pre, h_out, y_out};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4)) return SNR_ERR_ALIGN;
+    const int64_t tb = rows * n * 4, gb = n * 4;
+    // y_out may overlap nothing; h_out may only coincide exactly with r.
+    if (overlaps(y_out, tb, a, tb) || overlaps(y_out, tb, r, tb) ||
+        overlaps(y_out, tb, h_out, tb) || overlaps(y_out, tb, gamma_post, gb) ||
+        overlaps(y_out, tb, gamma_pre, gb))
+        return SNR_ERR_ALIAS;
+    if (overlaps(h_out, tb, a, tb) || overlaps(h_out, tb, gamma_post, gb) ||
+        overlaps(h_out, tb, gamma_pre, gb))
+        return SNR_ERR_ALIAS;
+    if (h_out != r && overlaps(h_out, tb, r, tb)) return SNR_ERR_ALIAS;
+
+    bool vec = n % 4 == 0;
+    for (const void *p : ptrs) vec = vec && aligned(p, 16);
+    RowArgs args{};
+    args.x0 = a;
+    args.x1 = r;
+    args.g0 = gamma_post;
+    args.g1 = gamma_pre;
+    args.out0 = h_out;
+    args.out1 = y_out;
+    args.eps0 = eps_post;
+    args.eps1 = eps_pre;
+    args.rows = rows;
+    args.n = (int32_t)n;
+    return launch(OP_TAIL, ST_F32, 4, args, vec, stream);
+}
+
+const char *snr_strerror(int code) {
+    switch (code) {
+    case SNR_OK: return "success";
+    case SNR_ERR_NULL: return "a required pointer is NULL";
+    case SNR_ERR_SHAPE:
+        return "invalid shape (n < 1, n > 2^31-1, rows < 0, size overflow, "
+               "or a forced dispatch shape that cannot hold the row)";
+    case SNR_ERR_DTYPE: return "unsupported dtype";
+    case SNR_ERR_EPS: return "epsilon must be finite and > 0";
+    case SNR_ERR_ALIAS: return "output buffers overlap inputs or each other";
+    case SNR_ERR_ALIGN: return "pointer not aligned to its element size";
+    case SNR_ERR_WORKSPACE:
+        return "split-row workspace unavailable or row too wide for "
+               "co-resident workgroups";
+    case SNR_ERR_HIP: return "HIP runtime call failed";
+    case SNR_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    default: return "unknown error code";
+    }
+}
+
+int snr_last_hip_error(void) { return t_last_hip_error; }
+
+int snr_force_shape(int kind, int g, int vpt) {
+    if (kind != SNR_SHAPE_AUTO && kind != SNR_SHAPE_ROWTILE &&
+        kind != SNR_SHAPE_SPLIT)
+        return SNR_ERR_SHAPE;
+    t_force_kind = kind;
+    t_force_g = g;
+    t_force_vpt = vpt;
+    return SNR_OK;
+}
+
+int snr_last_shape(char *buf, int len) {
+    if (!buf || len <= 0) return SNR_ERR_NULL;
+    std::snprintf(buf, (size_t)len, "%s", t_last_shape);
+    return SNR_OK;
+}
+
+int snr_split_timeouts(hipStream_t stream, int64_t *count) {
+    if (!count) return SNR_ERR_NULL;
+    *count = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    Workspace w;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        auto it = g_ws.find(std::make_pair(dev, stream));
+        if (it == g_ws.end()) return SNR_OK;
+        w = it->second;
+    }
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    unsigned int host = 0;
+    e = hipMemcpy(&host, w.st.timeouts, sizeof host, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    *count = host;
+    if (host != 0) {
+        // A wait that gave up may leave published slots behind: clear the
+        // whole workspace so the next launch starts from zero.
+        e = zero_words(w.base, w.words, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SNR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// snr_internal.h - types shared by the kernel translation unit and the host
+// dispatch layer of libsnr. Not part of the public ABI (include/snr.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snr {
+
+enum Op : int { OP_PLAIN = 0, OP_TAIL = 1 };
+enum Storage : int { ST_F32 = 0, ST_BF16 = 1 };
+enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2 };
+
+// Everything a row kernel needs. For OP_PLAIN only x0, g0, out0 and eps0 are
+// used; for OP_TAIL: x0 = a, x1 = r, g0 = gamma_post, g1 = gamma_pre,
+// out0 = h, out1 = y, eps0 = eps_post, eps1 = eps_pre.
+struct RowArgs {
+    const void *x0;
+    const void *x1;
+    const void *g0;
+    const void *g1;
+    void *out0;
+    void *out1;
+    float eps0;
+    float eps1;
+    int64_t rows;  // rows in the whole tensor
+    int32_t n;     // elements per row
+    int32_t nv;    // loads per row (n / width)
+};
+
+// Cross-workgroup state of the split-row kernels (device memory, owned by a
+// per-(device, stream) workspace). Every field starts at zero and every
+// launch leaves it at zero again (see the split kernel).
+struct SplitState {
+    unsigned long long *slots;  // [2][slot_cap] published partial sums
+    unsigned int *depart;       // [2][row_cap] readers done per row
+    unsigned int *ticket;       // work-item ticket dispenser
+    unsigned int *timeouts;     // bounded-wait overruns (watchdog count)
+    int64_t slot_cap;           // capacity of one slot set
+    int64_t row_cap;            // capacity of one depart set
+    uint32_t spin_limit;        // polls before a wait gives up
+};
+
+// Chunk geometry of the split-row kernels: 256 threads per workgroup, each
+// holding `vpt` loads of the chunk.
+constexpr int kSplitBlock = 256;
+constexpr int kSplitMaxChunks = 1024;
+
+using RowtileLaunch = hipError_t (*)(const RowArgs &, int64_t row0,
+                                     int64_t nrows, hipStream_t);
+using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
+                                   int64_t row0, int64_t nrows, int chunks,
+                                   hipStream_t);
+using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
+
+struct KernelEntry {
+    int op;        // Op
+    int storage;   // Storage
+    int width;     // elements per load (4 or 8 for 128-bit, 1 otherwise)
+    int kind;      // Kind
+    int g;         // lanes per row (rowtile) / workgroup size (split)
+    int vpt;       // loads held per lane
+    int block;     // threads per workgroup
+    RowtileLaunch rowtile;
+    SplitLaunch split;
+    OccupancyQuery occupancy;
+};
+
+// The table of compiled kernels (defined in snr_kernels.hip).
+const KernelEntry *kernel_table(int *count);
+
+// Zero `words` 32-bit words with a kernel (used instead of a memset so that
+// the call can also be recorded into a HIP graph).
+hipError_t zero_words(void *p, int64_t words, hipStream_t stream);
+
+}  // namespace snr

@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol include/snr.h declares, and
+rejects bad arguments with the documented codes. CPU only: every call here
+fails validation before the library makes any HIP call (fake, never
+dereferenced addresses), so no GPU is touched."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from sandwich_norm_residual_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "snr.h")
+
+
+def _header_text():
+    with open(HEADER) as fh:
+        return fh.read()
+
+
+def declared_functions():
+    return set(re.findall(r"^SNR_API\s+[\w\s\*]*?\b(\w+)\s*\(", _header_text(), re.M))
+
+
+def header_enum(name):
+    m = re.search(rf"\b{name}\s*=\s*(\d+)", _header_text())
+    assert m, name
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_declares_the_two_entry_points():
+    fns = declared_functions()
+    assert {"rmsnorm_fwd", "sandwich_tail"} <= fns
+    assert fns == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = declared_functions() - exported
+    assert not missing, missing
+    for name in declared_functions():
+        assert getattr(L, name) is not None
+
+
+def test_error_codes_match_header():
+    for name in ["SNR_OK", "SNR_ERR_NULL", "SNR_ERR_SHAPE", "SNR_ERR_DTYPE",
+                 "SNR_ERR_EPS", "SNR_ERR_ALIAS", "SNR_ERR_ALIGN",
+                 "SNR_ERR_WORKSPACE", "SNR_ERR_HIP", "SNR_ERR_DEVICE",
+                 "SNR_F32", "SNR_BF16"]:
+        assert header_enum(name) == getattr(_lib, name), name
+    assert header_enum("SNR_SHAPE_ROWTILE") == _lib.SHAPE_ROWTILE
+    assert header_enum("SNR_SHAPE_SPLIT") == _lib.SHAPE_SPLIT
+
+
+def test_strerror_covers_every_code(L):
+    seen = set()
+    for code in range(10):
+        text = _lib.strerror(code)
+        assert text and text != "unknown error code", code
+        seen.add(text)
+    assert len(seen) == 10
+    assert _lib.strerror(12345) == "unknown error code"
+
+
+BASE = 1 << 32          # fake device addresses, 16-byte aligned, never used
+GAM = BASE + (1 << 28)
+OUT = BASE + (1 << 29)
+
+
+def plain(x=BASE, g=GAM, eps=1e-5, rows=4, n=64, dtype=_lib.SNR_F32, y=OUT):
+    return _lib.rmsnorm_fwd(x, g, eps, rows, n, dtype, y, 0)
+
+
+def tail(a=BASE, r=BASE + (1 << 26), gp=GAM, ep=1e-8, gq=GAM + (1 << 20),
+         eq=1e-5, h=OUT, y=OUT + (1 << 26), rows=4, n=64):
+    return _lib.sandwich_tail(a, r, gp, ep, gq, eq, h, y, rows, n, 0)
+
+
+def test_plain_argument_errors(L):
+    assert plain(x=0) == _lib.SNR_ERR_NULL
+    assert plain(g=0) == _lib.SNR_ERR_NULL
+    assert plain(y=0) == _lib.SNR_ERR_NULL
+    assert plain(n=0) == _lib.SNR_ERR_SHAPE
+    assert plain(n=-3) == _lib.SNR_ERR_SHAPE
+    assert plain(n=2 ** 31) == _lib.SNR_ERR_SHAPE
+    assert plain(rows=-1) == _lib.SNR_ERR_SHAPE
+    assert plain(rows=2 ** 62, n=2 ** 20) == _lib.SNR_ERR_SHAPE
+    assert plain(dtype=2) == _lib.SNR_ERR_DTYPE
+    assert plain(dtype=-1) == _lib.SNR_ERR_DTYPE
+    for bad in (0.0, -1e-5, math.nan, math.inf, -math.inf):
+        assert plain(eps=bad) == _lib.SNR_ERR_EPS, bad
+    assert plain(x=BASE + 2) == _lib.SNR_ERR_ALIGN
+    assert plain(y=OUT + 1, dtype=_lib.SNR_BF16) == _lib.SNR_ERR_ALIGN
+    # y partially overlapping x, or overlapping gamma
+    assert plain(y=BASE + 4) == _lib.SNR_ERR_ALIAS
+    assert plain(y=GAM - 8) == _lib.SNR_ERR_ALIAS
+    assert plain(x=GAM, y=GAM) == _lib.SNR_ERR_ALIAS  # in place over gamma
+
+
+def test_plain_rows_zero_is_a_noop_even_with_null_pointers(L):
+    assert plain(x=0, g=0, y=0, rows=0) == _lib.SNR_OK
+
+
+def test_tail_argument_errors(L):
+    assert tail(a=0) == _lib.SNR_ERR_NULL
+    assert tail(y=0) == _lib.SNR_ERR_NULL
+    assert tail(n=0) == _lib.SNR_ERR_SHAPE
+    assert tail(rows=-2) == _lib.SNR_ERR_SHAPE
+    assert tail(ep=0.0) == _lib.SNR_ERR_EPS
+    assert tail(eq=math.nan) == _lib.SNR_ERR_EPS
+    assert tail(h=OUT + 2) == _lib.SNR_ERR_ALIGN
+    r = BASE + (1 << 26)
+    assert tail(h=BASE) == _lib.SNR_ERR_ALIAS           # h over a
+    assert tail(y=r) == _lib.SNR_ERR_ALIAS              # y over r
+    assert tail(y=OUT) == _lib.SNR_ERR_ALIAS            # y over h
+    assert tail(h=r + 16) == _lib.SNR_ERR_ALIAS         # h partly over r
+    assert tail(y=GAM) == _lib.SNR_ERR_ALIAS            # y over a gain
+    assert tail(h=GAM + (1 << 20) - 4) == _lib.SNR_ERR_ALIAS  # h over gamma_pre
+    assert tail(a=0, r=0, gp=0, gq=0, h=0, y=0, rows=0) == _lib.SNR_OK
+
+
+def test_force_shape_rejects_unknown_kind(L):
+    assert L.snr_force_shape(7, 0, 0) == _lib.SNR_ERR_SHAPE
+    assert L.snr_force_shape(_lib.SHAPE_AUTO, 0, 0) == _lib.SNR_OK
+    buf = ctypes.create_string_buffer(8)
+    assert L.snr_last_shape(None, 8) == _lib.SNR_ERR_NULL
+    assert L.snr_last_shape(buf, 8) == _lib.SNR_OK

@@ -1,0 +1,331 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the f64 oracle on
+the same seeded inputs, element by element.
+
+Covers every configuration at full size in the launch configuration the
+benchmark times (automatic shape choice), every compiled dispatch shape forced
+on rows it is not normally chosen for (ragged within its tile), the split-row
+path with 1..5 chunks, ragged and misaligned rows, in-place operation,
+sentinel prefill, determinism, rows = 0, and bf16 round-to-nearest-even.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import sandwich_norm_residual_amd as snr  # noqa: E402
+from sandwich_norm_residual_amd import _lib  # noqa: E402
+from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
+from parity import (TOL_BF16, TOL_F32, bf16_as_f64, plain_error,  # noqa: E402
+                    tail_errors)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# Row-tile shapes compiled for every (operation, storage, width); 1024 x 16
+# exists only where the row fits the registers of a 1024-lane workgroup.
+ROWTILE_SHAPES = [(1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (32, 4),
+                  (64, 2), (64, 4), (64, 8), (64, 16), (128, 8), (128, 13),
+                  (128, 16), (256, 4), (256, 7), (256, 8), (256, 16),
+                  (512, 4), (512, 8), (512, 16), (1024, 2), (1024, 4),
+                  (1024, 8)]
+WIDE_EXTRA = {("plain", "f32", 4), ("plain", "f32", 1), ("plain", "bf16", 1),
+              ("tail", "f32", 1)}
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def dev_bf16(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
+    return t.to(DEV).view(torch.bfloat16)
+
+
+def host_f64(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_as_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_plain(inp, prefill=float("nan"), out_is_x=False):
+    bf16 = inp["x"].dtype == np.uint16
+    x = dev_bf16(inp["x"]) if bf16 else dev_f32(inp["x"])
+    g = dev_bf16(inp["gamma"]) if bf16 else dev_f32(inp["gamma"])
+    out = x if out_is_x else torch.full_like(x, prefill)
+    snr.rmsnorm_fwd(x, g, inp["eps"], out=out)
+    torch.cuda.synchronize()
+    return host_f64(out), out
+
+
+def run_tail(inp, prefill=float("nan"), in_place=False):
+    a, r = dev_f32(inp["a"]), dev_f32(inp["r"])
+    gp, gq = dev_f32(inp["gamma_post"]), dev_f32(inp["gamma_pre"])
+    h = r if in_place else torch.full_like(a, prefill)
+    y = torch.full_like(a, prefill)
+    snr.sandwich_tail(a, r, gp, inp["eps_post"], gq, inp["eps_pre"],
+                      h_out=h, y_out=y)
+    torch.cuda.synchronize()
+    return host_f64(h), host_f64(y)
+
+
+def check_plain(oracle, inp, got, label):
+    want = oracle.rmsnorm(inp["x"], inp["gamma"], inp["eps"])
+    tol = TOL_BF16 if inp["x"].dtype == np.uint16 else TOL_F32
+    err = plain_error(got, want)
+    say(f"{label}: max rel err {err:.3e} (tol {tol:g}) shape {snr.last_shape()}")
+    assert err <= tol, (label, err)
+    return err
+
+
+def check_tail(oracle, inp, h, y, label):
+    o = oracle.sandwich_tail(inp["a"], inp["r"], inp["gamma_post"],
+                             inp["eps_post"], inp["gamma_pre"], inp["eps_pre"])
+    eh, ey = tail_errors(h, y, o, inp["r"], inp["gamma_pre"])
+    say(f"{label}: h err {eh:.3e} y err {ey:.3e} shape {snr.last_shape()}")
+    assert eh <= TOL_F32 and ey <= TOL_F32, (label, eh, ey)
+
+
+# ---------------------------------------------------------------------------
+# Every configuration, full size, automatic shape (what the benchmark runs)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(gen.CONFIGS))
+def test_config_full_size(oracle, name):
+    cfg = gen.CONFIGS[name]
+    say(f"config {name} rows={cfg.rows} n={cfg.n} {cfg.dtype}")
+    inp = gen.make(cfg)
+    if cfg.kind == "plain":
+        got, _ = run_plain(inp)
+        check_plain(oracle, inp, got, name)
+    else:
+        h, y = run_tail(inp)
+        check_tail(oracle, inp, h, y, name)
+
+
+# ---------------------------------------------------------------------------
+# Every compiled shape, forced, on a row that leaves part of its tile empty
+# ---------------------------------------------------------------------------
+def _shape_cases():
+    cases = []
+    for op in ("plain", "tail"):
+        combos = [("f32", 4), ("f32", 1)]
+        if op == "plain":
+            combos += [("bf16", 8), ("bf16", 1)]
+        for st, w in combos:
+            shapes = list(ROWTILE_SHAPES)
+            if (op, st, w) in WIDE_EXTRA:
+                shapes.append((1024, 16))
+            for g, vpt in shapes:
+                cases.append((op, st, w, g, vpt))
+    return cases
+
+
+def _case_id(c):
+    return "{}-{}-w{}-g{}-v{}".format(*c)
+
+
+@pytest.mark.parametrize("case", _shape_cases(), ids=_case_id)
+def test_forced_rowtile_shape(oracle, case):
+    op, st, w, g, vpt = case
+    cap = g * vpt
+    nv = max(1, cap - g // 2 - (1 if g == 1 else 0))   # ragged in the tile
+    n = nv * w
+    while w == 1 and n % 4 == 0:   # keep rows off the 128-bit path
+        n -= 1
+    rows = 37
+    seed = 1000 + g * 31 + vpt
+    say(f"forced rowtile {_case_id(case)} rows={rows} n={n}")
+    with snr.forced_shape("rowtile", g, vpt):
+        if op == "plain":
+            inp = gen.random_plain(rows, n, seed, dtype=st)
+            got, _ = run_plain(inp)
+            shape = snr.last_shape()
+            check_plain(oracle, inp, got, _case_id(case))
+        else:
+            inp = gen.random_tail(rows, n, seed)
+            h, y = run_tail(inp)
+            shape = snr.last_shape()
+            check_tail(oracle, inp, h, y, _case_id(case))
+    assert shape == f"rowtile:{g}:{vpt}:{w}", shape
+
+
+@pytest.mark.parametrize("op", ["plain", "tail"])
+@pytest.mark.parametrize("w", [4, 1])
+@pytest.mark.parametrize("chunks_nv", [(1, 100), (3, 2 * 2048 + 5),
+                                       (5, 5 * 2048)])
+def test_forced_split(oracle, op, w, chunks_nv):
+    chunks, nv = chunks_nv
+    # element-wide rows: a width that is not a multiple of 4
+    n = nv * 4 if w == 4 else (nv if nv % 4 else nv - 1)
+    rows = 7
+    say(f"forced split op={op} w={w} chunks={chunks} rows={rows} n={n}")
+    with snr.forced_shape("split", 0, 8):
+        if op == "plain":
+            inp = gen.random_plain(rows, n, 77 + chunks)
+            got, _ = run_plain(inp)
+            shape = snr.last_shape()
+            check_plain(oracle, inp, got, f"split-{op}-w{w}-c{chunks}")
+        else:
+            inp = gen.random_tail(rows, n, 78 + chunks)
+            h, y = run_tail(inp)
+            shape = snr.last_shape()
+            check_tail(oracle, inp, h, y, f"split-{op}-w{w}-c{chunks}")
+    assert shape == f"split:256:8:{w}:{chunks}", shape
+    assert snr.split_timeouts() == 0
+
+
+def test_forced_shape_that_cannot_hold_the_row_is_refused():
+    x = torch.zeros(4, 4096, device=DEV)
+    g = torch.ones(4096, device=DEV)
+    with snr.forced_shape("rowtile", 64, 2):
+        with pytest.raises(snr.SnrError) as ei:
+            snr.rmsnorm_fwd(x, g, 1e-5)
+    assert ei.value.code == _lib.SNR_ERR_SHAPE
+    with snr.forced_shape("rowtile", 3, 4):
+        with pytest.raises(snr.SnrError):
+            snr.rmsnorm_fwd(x, g, 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Ragged and misaligned rows, automatic shape
+# ---------------------------------------------------------------------------
+RAGGED_N = [1, 2, 3, 4, 5, 7, 8, 63, 65, 127, 129, 255, 257, 1000, 1023,
+            4097, 6657, 16385, 33333, 100003]
+
+
+@pytest.mark.parametrize("n", RAGGED_N)
+def test_ragged_plain(oracle, n):
+    rows = 67
+    say(f"ragged plain rows={rows} n={n}")
+    inp = gen.random_plain(rows, n, 3000 + n, lo=-6, hi=4)
+    got, _ = run_plain(inp)
+    check_plain(oracle, inp, got, f"ragged-plain-{n}")
+    inpb = gen.random_plain(rows, n, 4000 + n, dtype="bf16")
+    gotb, _ = run_plain(inpb)
+    check_plain(oracle, inpb, gotb, f"ragged-plain-bf16-{n}")
+
+
+@pytest.mark.parametrize("n", RAGGED_N)
+def test_ragged_tail(oracle, n):
+    rows = 29
+    say(f"ragged tail rows={rows} n={n}")
+    inp = gen.random_tail(rows, n, 5000 + n)
+    h, y = run_tail(inp)
+    check_tail(oracle, inp, h, y, f"ragged-tail-{n}")
+
+
+@pytest.mark.parametrize("n", [6656, 768, 4096])
+def test_misaligned_base_pointer(oracle, n):
+    """A view one element into its allocation is not 16-byte aligned: the
+    element-wide path must run and agree."""
+    rows = 16
+    say(f"misaligned rows={rows} n={n}")
+    inp = gen.random_plain(rows, n, 6000 + n)
+    buf = torch.empty(rows * n + 1, device=DEV)
+    x = buf[1:].view(rows, n)
+    x.copy_(dev_f32(inp["x"]))
+    gbuf = torch.empty(n + 1, device=DEV)
+    g = gbuf[1:]
+    g.copy_(dev_f32(inp["gamma"]))
+    ybuf = torch.full((rows * n + 1,), float("nan"), device=DEV)
+    y = ybuf[1:].view(rows, n)
+    snr.rmsnorm_fwd(x, g, inp["eps"], out=y)
+    torch.cuda.synchronize()
+    assert snr.last_shape().endswith(":1"), snr.last_shape()
+    check_plain(oracle, inp, host_f64(y), f"misaligned-{n}")
+    # the same rows from an aligned allocation take the 128-bit path
+    got, _ = run_plain(inp)
+    assert snr.last_shape().endswith(":4")
+    check_plain(oracle, inp, got, f"aligned-{n}")
+
+
+# ---------------------------------------------------------------------------
+# In place, sentinels, determinism, rows = 0, streams
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [6656, 6657, 65536, 3])
+def test_in_place(oracle, n):
+    rows = 9
+    say(f"in-place rows={rows} n={n}")
+    inp = gen.random_plain(rows, n, 7000 + n)
+    got, _ = run_plain(inp, out_is_x=True)
+    check_plain(oracle, inp, got, f"in-place-plain-{n}")
+    tin = gen.random_tail(rows, n, 7100 + n)
+    h, y = run_tail(tin, in_place=True)
+    check_tail(oracle, tin, h, y, f"in-place-tail-{n}")
+
+
+@pytest.mark.parametrize("prefill", [float("nan"), -999.0])
+@pytest.mark.parametrize("n", [2, 3, 6657, 65536])
+def test_sentinel_prefill_is_overwritten(oracle, prefill, n):
+    rows = 5
+    say(f"sentinel {prefill} rows={rows} n={n}")
+    inp = gen.random_plain(rows, n, 8000 + n)
+    got, _ = run_plain(inp, prefill=prefill)
+    assert not np.any(got == prefill) or prefill != prefill
+    assert np.all(np.isfinite(got))
+    check_plain(oracle, inp, got, f"sentinel-{n}")
+    tin = gen.random_tail(rows, n, 8100 + n)
+    h, y = run_tail(tin, prefill=prefill)
+    assert np.all(np.isfinite(h)) and np.all(np.isfinite(y))
+    check_tail(oracle, tin, h, y, f"sentinel-tail-{n}")
+
+
+@pytest.mark.parametrize("name", ["tail_4096x6656_f32", "edge_256x65536_f32",
+                                  "plain_16384x4096_bf16", "edge_256x3_f32"])
+def test_bitwise_deterministic(name):
+    cfg = gen.CONFIGS[name]
+    say(f"determinism {name}")
+    inp = gen.make(cfg)
+    if cfg.kind == "plain":
+        a, _ = run_plain(inp)
+        b, _ = run_plain(inp)
+        assert np.array_equal(a, b)
+    else:
+        h1, y1 = run_tail(inp)
+        h2, y2 = run_tail(inp)
+        assert np.array_equal(h1, h2) and np.array_equal(y1, y2)
+
+
+def test_rows_zero_is_a_noop():
+    say("rows=0")
+    x = torch.empty(0, 64, device=DEV)
+    g = torch.ones(64, device=DEV)
+    y = snr.rmsnorm_fwd(x, g, 1e-5)
+    assert y.shape == (0, 64)
+    h, yy = snr.sandwich_tail(x, x, g, 1e-8, g, 1e-5)
+    assert h.shape == (0, 64) and yy.shape == (0, 64)
+
+
+def test_non_default_stream(oracle):
+    say("non-default stream")
+    inp = gen.make("tail_8x6656_f32")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a, r = dev_f32(inp["a"]), dev_f32(inp["r"])
+        gp, gq = dev_f32(inp["gamma_post"]), dev_f32(inp["gamma_pre"])
+        h, y = snr.sandwich_tail(a, r, gp, inp["eps_post"], gq,
+                                 inp["eps_pre"])
+    s.synchronize()
+    check_tail(oracle, inp, host_f64(h), host_f64(y), "stream")
+
+
+def test_bf16_output_is_round_to_nearest_even(oracle):
+    """8e-3 cannot tell rounding from truncation (both stay within one bf16
+    unit), so check the rounding itself: almost every output equals the
+    oracle's value rounded to nearest-even, and none is more than one bf16
+    unit away."""
+    say("bf16 rounding")
+    inp = gen.make("plain_16384x4096_bf16", rows=512)
+    x, g = dev_bf16(inp["x"]), dev_bf16(inp["gamma"])
+    y = snr.rmsnorm_fwd(x, g, inp["eps"])
+    torch.cuda.synchronize()
+    bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.rmsnorm(inp["x"], inp["gamma"], inp["eps"])
+    want_bits = gen.f32_to_bf16_bits(want.astype(np.float32))
+    ulps = np.abs(bits.astype(np.int32) - want_bits.astype(np.int32))
+    # same sign everywhere (the sign bit would make the difference huge)
+    assert ulps.max() <= 1, ulps.max()
+    assert np.mean(ulps == 0) >= 0.999, np.mean(ulps == 0)
