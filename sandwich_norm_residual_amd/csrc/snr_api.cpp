@@ -106,9 +106,8 @@ int get_workspace(int dev, hipStream_t stream, SplitState *out) {
         char *b = static_cast<char *>(w.base);
         w.st.slots = reinterpret_cast<unsigned long long *>(b);
         w.st.depart = reinterpret_cast<unsigned int *>(b + slot_bytes);
-        w.st.ticket =
+        w.st.timeouts =
             reinterpret_cast<unsigned int *>(b + slot_bytes + depart_bytes);
-        w.st.timeouts = w.st.ticket + 16;
         w.st.slot_cap = kSlotCap;
         w.st.row_cap = kRowCap;
         w.st.spin_limit = kSpinLimit;
@@ -157,15 +156,12 @@ const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
     return nullptr;
 }
 
-constexpr int64_t kSplitAbove = 8192;  // loads per row above which rows split
-
 int split_chunks(const KernelEntry *k, int64_t nv) {
     const int64_t per = (int64_t)kSplitBlock * k->vpt;
     return (int)((nv + per - 1) / per);
 }
 
-int choose(int op, int st, int w, int64_t nv, int64_t rows,
-           const DeviceInfo &dev, Choice *c) {
+int choose(int op, int st, int w, int64_t nv, Choice *c) {
     if (t_force_kind == SNR_SHAPE_ROWTILE) {
         c->k = find_entry(op, st, w, KIND_ROWTILE, t_force_g, t_force_vpt);
         if (!c->k || (int64_t)c->k->g * c->k->vpt < nv) return SNR_ERR_SHAPE;
@@ -177,55 +173,33 @@ int choose(int op, int st, int w, int64_t nv, int64_t rows,
         c->chunks = split_chunks(c->k, nv);
         return SNR_OK;
     }
-    if (nv > kSplitAbove) {
-        c->k = find_entry(op, st, w, KIND_SPLIT, 0, 8);
-        if (!c->k) return SNR_ERR_SHAPE;
-        c->chunks = split_chunks(c->k, nv);
-        return SNR_OK;
-    }
     if (nv <= 128) {
         int g = 1;
         while (g * 4 < nv) g *= 2;
         c->k = find_entry(op, st, w, KIND_ROWTILE, g, 4);
         return c->k ? SNR_OK : SNR_ERR_SHAPE;
     }
-    if (nv <= 1024) {
-        int vpt = 2;
-        while (64 * vpt < nv) vpt *= 2;
-        c->k = find_entry(op, st, w, KIND_ROWTILE, 64, vpt);
-        return c->k ? SNR_OK : SNR_ERR_SHAPE;
-    }
-    // One workgroup per row: the smallest register tile that holds the row;
-    // among equal tiles the widest workgroup. When the rows alone cannot
-    // fill the chip (fewer than 4 wavefronts per CU), use the widest
-    // workgroup that holds the row so each row is fetched by more lanes.
+    // Wider rows: about two loads per lane, so each row is fetched by as
+    // many lanes as possible (G = nv/2 rounded up to a power of two, 64 to
+    // 1024 lanes), with the smallest compiled register tile that holds it.
+    int g = 64;
+    while (g < 1024 && 2LL * g < nv) g *= 2;
     int count = 0;
     const KernelEntry *t = kernel_table(&count);
     const KernelEntry *best = nullptr;
     for (int i = 0; i < count; ++i) {
         const KernelEntry &e = t[i];
         if (e.op != op || e.storage != st || e.width != w ||
-            e.kind != KIND_ROWTILE || e.g < 128)
+            e.kind != KIND_ROWTILE || e.g != g || (int64_t)e.g * e.vpt < nv)
             continue;
-        const int64_t cap = (int64_t)e.g * e.vpt;
-        if (cap < nv) continue;
-        if (!best) { best = &e; continue; }
-        const int64_t bcap = (int64_t)best->g * best->vpt;
-        if (cap < bcap || (cap == bcap && e.g > best->g)) best = &e;
+        if (!best || e.vpt < best->vpt) best = &e;
     }
-    if (!best) return SNR_ERR_SHAPE;
-    const int64_t waves = rows * (best->g / 64);
-    if (waves < 4LL * dev.cus) {
-        const KernelEntry *wide = nullptr;
-        for (int i = 0; i < count; ++i) {
-            const KernelEntry &e = t[i];
-            if (e.op != op || e.storage != st || e.width != w ||
-                e.kind != KIND_ROWTILE || e.g != 1024)
-                continue;
-            if ((int64_t)e.g * e.vpt < nv) continue;
-            if (!wide || e.vpt < wide->vpt) wide = &e;
-        }
-        if (wide) best = wide;
+    if (!best) {
+        // no register tile holds the row: split it across workgroups
+        c->k = find_entry(op, st, w, KIND_SPLIT, 0, 8);
+        if (!c->k) return SNR_ERR_SHAPE;
+        c->chunks = split_chunks(c->k, nv);
+        return SNR_OK;
     }
     c->k = best;
     return SNR_OK;
@@ -245,7 +219,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     RowArgs a = args_in;
     a.nv = (int32_t)(a.n / w);
     Choice c;
-    rc = choose(op, st, w, a.nv, a.rows, info, &c);
+    rc = choose(op, st, w, a.nv, &c);
     if (rc != SNR_OK) return rc;
     const KernelEntry *k = c.k;
 
@@ -263,7 +237,10 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         int per_cu = 0;
         hipError_t e = k->occupancy(&per_cu);
         if (e != hipSuccess) return hip_fail(e);
-        if ((int64_t)per_cu * info.cus < c.chunks) return SNR_ERR_WORKSPACE;
+        // Every workgroup of the cooperative grid must be co-resident: at
+        // most floor(capacity / chunks) rows are in flight at once.
+        const int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
+        if (max_groups < 1) return SNR_ERR_WORKSPACE;
         SplitState ws;
         rc = get_workspace(dev, stream, &ws);
         if (rc != SNR_OK) return rc;
@@ -271,7 +248,8 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         if (step > kRowCap) step = kRowCap;
         for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
             const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
-            e = k->split(a, ws, r0, nr, c.chunks, stream);
+            const int groups = (int)(nr < max_groups ? nr : max_groups);
+            e = k->split(a, ws, r0, nr, c.chunks, groups, stream);
             if (e != hipSuccess) return hip_fail(e);
         }
     }

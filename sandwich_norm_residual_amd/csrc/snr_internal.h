@@ -34,7 +34,6 @@ struct RowArgs {
 struct SplitState {
     unsigned long long *slots;  // [2][slot_cap] published partial sums
     unsigned int *depart;       // [2][row_cap] readers done per row
-    unsigned int *ticket;       // work-item ticket dispenser
     unsigned int *timeouts;     // bounded-wait overruns (watchdog count)
     int64_t slot_cap;           // capacity of one slot set
     int64_t row_cap;            // capacity of one depart set
@@ -50,7 +49,7 @@ using RowtileLaunch = hipError_t (*)(const RowArgs &, int64_t row0,
                                      int64_t nrows, hipStream_t);
 using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
                                    int64_t row0, int64_t nrows, int chunks,
-                                   hipStream_t);
+                                   int groups, hipStream_t);
 using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
 
 struct KernelEntry {

@@ -26,11 +26,11 @@
 // * Split-row kernel for very wide rows: one workgroup per chunk of a row. A
 //   workgroup publishes its chunk's partial sum to device memory, waits for
 //   the other chunks of its row, adds the partials in chunk order and
-//   normalises its chunk from registers (no second read of the row). Chunks
-//   are handed out by an atomic ticket in the order workgroups start, so a
-//   waiting workgroup only ever waits for chunks that have already started
-//   or will be given to the next workgroup to start: with at least `chunks`
-//   workgroups co-resident there is no deadlock.
+//   normalises its chunk from registers (no second read of the row). The
+//   grid is a cooperative launch (every workgroup co-resident) of `groups`
+//   x `chunks` workgroups; workgroup (g, c) handles chunk c of rows g,
+//   g + groups, g + 2 groups, ... in order, so a wait only ever depends on
+//   resident workgroups that are working on the same row.
 // * Stores of outputs and loads of row data are non-temporal (each byte is
 //   touched once); gains use ordinary cached loads (every row re-reads them).
 #include <hip/hip_runtime.h>
@@ -376,102 +376,94 @@ __device__ float cross_chunk_total(float partial, const SplitState &st,
 template <int OP, int ST, int W, int VPT>
 __global__ void __launch_bounds__(SB)
 split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
-             int chunks) {
+             int chunks, int groups) {
     using A = Access<ST, W>;
     using T = typename A::T;
     __shared__ float red[2][SNW];
     __shared__ float part[kSplitMaxChunks];
-    __shared__ unsigned int s_item;
 
     const int tid = threadIdx.x;
-    const int64_t items = nrows * (int64_t)chunks;
-    if (tid == 0) {
-        const unsigned int t = __hip_atomic_fetch_add(
-            st.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // The holder of the last ticket knows every ticket has been drawn.
-        if ((int64_t)t == items - 1)
-            __hip_atomic_store(st.ticket, 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        s_item = t;
-    }
-    __syncthreads();
-    const int64_t item = s_item;
-    const int64_t rl = item / chunks;
-    const int chunk = (int)(item - rl * chunks);
-    const int64_t off = (row0 + rl) * (int64_t)p.n;
+    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
+    const int group = (int)(blockIdx.x / (unsigned)chunks);
     const int first = chunk * (SB * VPT) + tid;
     const int nv = p.nv;
-
-    float v0[VPT][W];
-    float v1[OP == OP_TAIL ? VPT : 1][W];
-    (void)v1;
-    const T *x0 = static_cast<const T *>(p.x0) + off;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int i = first + k * SB;
-        if (i < nv) A::load_nt(x0, i, v0[k]); else zero(v0[k]);
-    }
-    if constexpr (OP == OP_TAIL) {
-        const T *x1 = static_cast<const T *>(p.x1) + off;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = first + k * SB;
-            if (i < nv) A::load_nt(x1, i, v1[k]); else zero(v1[k]);
-        }
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) s += sumsq<W>(v0[k]);
-    const float tot0 = cross_chunk_total(block_total(s, red[0]), st, 0, rl,
-                                         chunk, chunks, part);
-    const float inv0 = inv_rms(tot0, p.n, p.eps0);
-
     const T *g0 = static_cast<const T *>(p.g0);
-    T *out0 = static_cast<T *>(p.out0) + off;
-    if constexpr (OP == OP_PLAIN) {
+    const T *g1 = static_cast<const T *>(p.g1);
+
+    for (int64_t rl = group; rl < nrows; rl += groups) {
+        const int64_t off = (row0 + rl) * (int64_t)p.n;
+        float v0[VPT][W];
+        float v1[OP == OP_TAIL ? VPT : 1][W];
+        (void)v1;
+        const T *x0 = static_cast<const T *>(p.x0) + off;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int i = first + k * SB;
-            if (i < nv) {
-                float g[W], o[W];
-                A::load(g0, i, g);
+            if (i < nv) A::load_nt(x0, i, v0[k]); else zero(v0[k]);
+        }
+        if constexpr (OP == OP_TAIL) {
+            const T *x1 = static_cast<const T *>(p.x1) + off;
 #pragma unroll
-                for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
-                A::store_nt(out0, i, o);
+            for (int k = 0; k < VPT; ++k) {
+                const int i = first + k * SB;
+                if (i < nv) A::load_nt(x1, i, v1[k]); else zero(v1[k]);
             }
         }
-    } else {
+        float s = 0.0f;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = first + k * SB;
-            if (i < nv) {
-                float g[W];
-                A::load(g0, i, g);
+        for (int k = 0; k < VPT; ++k) s += sumsq<W>(v0[k]);
+        const float tot0 = cross_chunk_total(block_total(s, red[0]), st, 0, rl,
+                                             chunk, chunks, part);
+        const float inv0 = inv_rms(tot0, p.n, p.eps0);
+
+        T *out0 = static_cast<T *>(p.out0) + off;
+        if constexpr (OP == OP_PLAIN) {
 #pragma unroll
-                for (int e = 0; e < W; ++e)
-                    v1[k][e] = fmaf(v0[k][e] * inv0, g[e], v1[k][e]);
-                A::store_nt(out0, i, v1[k]);
+            for (int k = 0; k < VPT; ++k) {
+                const int i = first + k * SB;
+                if (i < nv) {
+                    float g[W], o[W];
+                    A::load(g0, i, g);
+#pragma unroll
+                    for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
+                    A::store_nt(out0, i, o);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int i = first + k * SB;
+                if (i < nv) {
+                    float g[W];
+                    A::load(g0, i, g);
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        v1[k][e] = fmaf(v0[k][e] * inv0, g[e], v1[k][e]);
+                    A::store_nt(out0, i, v1[k]);
+                }
+            }
+            float sh = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) sh += sumsq<W>(v1[k]);
+            const float tot1 = cross_chunk_total(block_total(sh, red[1]), st,
+                                                 1, rl, chunk, chunks, part);
+            const float inv1 = inv_rms(tot1, p.n, p.eps1);
+            T *out1 = static_cast<T *>(p.out1) + off;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int i = first + k * SB;
+                if (i < nv) {
+                    float g[W], o[W];
+                    A::load(g1, i, g);
+#pragma unroll
+                    for (int e = 0; e < W; ++e) o[e] = v1[k][e] * inv1 * g[e];
+                    A::store_nt(out1, i, o);
+                }
             }
         }
-        float sh = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) sh += sumsq<W>(v1[k]);
-        const float tot1 = cross_chunk_total(block_total(sh, red[1]), st, 1,
-                                             rl, chunk, chunks, part);
-        const float inv1 = inv_rms(tot1, p.n, p.eps1);
-        const T *g1 = static_cast<const T *>(p.g1);
-        T *out1 = static_cast<T *>(p.out1) + off;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = first + k * SB;
-            if (i < nv) {
-                float g[W], o[W];
-                A::load(g1, i, g);
-#pragma unroll
-                for (int e = 0; e < W; ++e) o[e] = v1[k][e] * inv1 * g[e];
-                A::store_nt(out1, i, o);
-            }
-        }
+        // The next row reuses `part` and `red`: every lane must have finished
+        // reading them (cross_chunk_total's sums) before they are rewritten.
+        __syncthreads();
     }
 }
 
@@ -506,12 +498,15 @@ hipError_t occupancy_rowtile(int *blocks_per_cu) {
 
 template <int OP, int ST, int W, int VPT>
 hipError_t launch_split(const RowArgs &p, const SplitState &st, int64_t row0,
-                        int64_t nrows, int chunks, hipStream_t stream) {
-    const int64_t blocks = nrows * (int64_t)chunks;
-    hipLaunchKernelGGL((split_kernel<OP, ST, W, VPT>),
-                       dim3((unsigned int)blocks), dim3(SB), 0, stream, p, st,
-                       row0, nrows, chunks);
-    return hipGetLastError();
+                        int64_t nrows, int chunks, int groups,
+                        hipStream_t stream) {
+    RowArgs pa = p;
+    SplitState sa = st;
+    int c = chunks, g = groups;
+    void *args[] = {&pa, &sa, &row0, &nrows, &c, &g};
+    return hipLaunchCooperativeKernel(
+        reinterpret_cast<const void *>(&split_kernel<OP, ST, W, VPT>),
+        dim3((unsigned int)(groups * chunks)), dim3(SB), args, 0, stream);
 }
 
 template <int OP, int ST, int W, int VPT>
