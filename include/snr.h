@@ -86,9 +86,9 @@ enum {
  *          with x or gamma is SNR_ERR_ALIAS.
  *   stream HIP stream to enqueue on (NULL = default stream)
  *
- * Pointers need only element alignment (4 B for f32, 2 B for bf16); 16-byte
- * aligned rows (and n a multiple of 4 for f32, 8 for bf16) select 128-bit
- * loads, anything else selects element-wide loads.
+ * Pointers need only element alignment (4 B for f32, 2 B for bf16). Rows
+ * are moved with 128-bit accesses whatever their alignment; the n % 4 (f32)
+ * or n % 8 (bf16) elements after a row's last whole vector one at a time.
  */
 SNR_API int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
                 int64_t n, int dtype, void *y, hipStream_t stream);
@@ -149,8 +149,10 @@ SNR_API int snr_last_hip_error(void);
  * snr_force_shape applies to subsequent calls on the calling thread until it
  * is called again with SNR_SHAPE_AUTO. A forced shape that cannot hold the
  * row (g * vpt loads < row length) or that has no compiled kernel returns
- * SNR_ERR_SHAPE from the call. snr_last_shape writes "kind:g:vpt:width" of the
- * calling thread's most recent successful launch into buf (NUL-terminated).
+ * SNR_ERR_SHAPE from the call. snr_last_shape writes "rowtile:g:vpt:width"
+ * or "split:256:vpt:width:chunks" (width = elements per 128-bit vector) of
+ * the calling thread's most recent successful launch into buf
+ * (NUL-terminated).
  */
 enum { SNR_SHAPE_AUTO = 0, SNR_SHAPE_ROWTILE = 1, SNR_SHAPE_SPLIT = 2 };
 SNR_API int snr_force_shape(int kind, int g, int vpt);
@@ -163,6 +165,11 @@ SNR_API int snr_last_shape(char *buf, int len);
  * workspace and finishes (its outputs are then invalid). This returns the
  * number of such events recorded on (current device, stream) and clears the
  * count. It synchronises the stream. 0 means every wait completed normally.
+ * When the count is not 0 the stream's workspace is cleared again before
+ * this returns, so later calls start from a clean state.
+ * The environment variable SNR_SPLIT_SPIN_LIMIT (a positive integer, read at
+ * each split-row launch) replaces the default bound of 2^22 polls; tests use
+ * a tiny value to force the bounded-wait path.
  */
 SNR_API int snr_split_timeouts(hipStream_t stream, int64_t *count);
 

@@ -158,7 +158,8 @@ const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
 
 int split_chunks(const KernelEntry *k, int64_t nv) {
     const int64_t per = (int64_t)kSplitBlock * k->vpt;
-    return (int)((nv + per - 1) / per);
+    const int64_t c = (nv + per - 1) / per;
+    return (int)(c > 0 ? c : 1);  // a row of only remainder elements
 }
 
 int choose(int op, int st, int w, int64_t nv, Choice *c) {
@@ -174,6 +175,7 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
         return SNR_OK;
     }
     if (nv <= 128) {
+        // several rows per wavefront: 4 vectors per lane
         int g = 1;
         while (g * 4 < nv) g *= 2;
         c->k = find_entry(op, st, w, KIND_ROWTILE, g, 4);
@@ -209,15 +211,18 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
 // Launch
 // ---------------------------------------------------------------------------
 int launch(int op, int st, int64_t esize, const RowArgs &args_in,
-           bool vec_ok, hipStream_t stream) {
+           hipStream_t stream) {
     int dev = 0;
     DeviceInfo info;
     int rc = current_device(&dev, &info);
     if (rc != SNR_OK) return rc;
 
-    const int w = vec_ok ? (int)(16 / esize) : 1;
+    // 128-bit vectors need only element alignment on gfx950; the n % w
+    // elements after a row's last whole vector are handled one by one.
+    const int w = (int)(16 / esize);
     RowArgs a = args_in;
     a.nv = (int32_t)(a.n / w);
+    a.rem = (int32_t)(a.n % w);
     Choice c;
     rc = choose(op, st, w, a.nv, &c);
     if (rc != SNR_OK) return rc;
@@ -244,6 +249,11 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         SplitState ws;
         rc = get_workspace(dev, stream, &ws);
         if (rc != SNR_OK) return rc;
+        // Test hook: a small poll budget forces the bounded-wait path.
+        if (const char *lim = std::getenv("SNR_SPLIT_SPIN_LIMIT")) {
+            const long v = std::strtol(lim, nullptr, 10);
+            if (v > 0) ws.spin_limit = (uint32_t)v;
+        }
         int64_t step = kSlotCap / c.chunks;
         if (step > kRowCap) step = kRowCap;
         for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
@@ -289,9 +299,6 @@ int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
     if (y != x && overlaps(y, tb, x, tb)) return SNR_ERR_ALIAS;
     if (overlaps(y, tb, gamma, gb)) return SNR_ERR_ALIAS;
 
-    const int w = (int)(16 / es);
-    const bool vec = n % w == 0 && aligned(x, 16) && aligned(y, 16) &&
-                     aligned(gamma, 16);
     RowArgs a{};
     a.x0 = x;
     a.g0 = gamma;
@@ -299,7 +306,7 @@ int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
     a.eps0 = eps;
     a.rows = rows;
     a.n = (int32_t)n;
-    return launch(OP_PLAIN, dtype == SNR_F32 ? ST_F32 : ST_BF16, es, a, vec,
+    return launch(OP_PLAIN, dtype == SNR_F32 ? ST_F32 : ST_BF16, es, a,
                   stream);
 }
 
@@ -327,8 +334,6 @@ int sandwich_tail(const float *a, const float *r, const float *gamma_post,
         return SNR_ERR_ALIAS;
     if (h_out != r && overlaps(h_out, tb, r, tb)) return SNR_ERR_ALIAS;
 
-    bool vec = n % 4 == 0;
-    for (const void *p : ptrs) vec = vec && aligned(p, 16);
     RowArgs args{};
     args.x0 = a;
     args.x1 = r;
@@ -340,7 +345,7 @@ int sandwich_tail(const float *a, const float *r, const float *gamma_post,
     args.eps1 = eps_pre;
     args.rows = rows;
     args.n = (int32_t)n;
-    return launch(OP_TAIL, ST_F32, 4, args, vec, stream);
+    return launch(OP_TAIL, ST_F32, 4, args, stream);
 }
 
 const char *snr_strerror(int code) {

@@ -25,7 +25,8 @@ struct RowArgs {
     float eps1;
     int64_t rows;  // rows in the whole tensor
     int32_t n;     // elements per row
-    int32_t nv;    // loads per row (n / width)
+    int32_t nv;    // whole 128-bit vectors per row (n / W)
+    int32_t rem;   // elements after the last whole vector (n % W)
 };
 
 // Cross-workgroup state of the split-row kernels (device memory, owned by a
@@ -55,7 +56,7 @@ using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
 struct KernelEntry {
     int op;        // Op
     int storage;   // Storage
-    int width;     // elements per load (4 or 8 for 128-bit, 1 otherwise)
+    int width;     // elements per 128-bit vector (4 f32, 8 bf16)
     int kind;      // Kind
     int g;         // lanes per row (rowtile) / workgroup size (split)
     int vpt;       // loads held per lane

@@ -10,8 +10,8 @@
 //
 // Design (HBM-bound, no contraction, so no MFMA):
 // * Each row is read from HBM exactly once: every lane loads its share of the
-//   row into registers with coalesced loads (128-bit when the row layout
-//   allows, element-wide otherwise), the sum of squares is reduced, and the
+//   row into registers with coalesced 128-bit loads (the n % W elements past
+//   the last whole vector one at a time), the sum of squares is reduced, and the
 //   normalise pass works from those registers. The tail also keeps h in
 //   registers for its second reduction, so a and r are read once and h and y
 //   written once.
@@ -41,51 +41,48 @@
 namespace snr {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // ---------------------------------------------------------------------------
-// Storage codecs: W elements per load, converted to f32 registers.
+// Storage codecs. Rows are moved with 128-bit accesses: W elements per
+// vector (4 f32 or 8 bf16). The vector types carry only element alignment:
+// gfx950 performs dwordx4 accesses at any 4-byte (f32) or 2-byte (bf16)
+// boundary, so rows whose start is not 16-byte aligned (odd n, offset views)
+// still use 128-bit accesses. The n % W elements after a row's last whole
+// vector are moved one at a time.
 // ---------------------------------------------------------------------------
-template <int ST, int W>
-struct Access;
+template <int ST>
+struct Codec;
 
 template <>
-struct Access<ST_F32, 4> {
+struct Codec<ST_F32> {
     using T = float;
+    static constexpr int W = 4;
+    typedef float vec __attribute__((ext_vector_type(4), aligned(4)));
     __device__ static void load_nt(const T *row, int i, float (&v)[4]) {
-        const f32x4 q = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(row) + i);
+        const vec q = __builtin_nontemporal_load(
+            reinterpret_cast<const vec *>(row) + i);
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
     __device__ static void load(const T *base, int i, float (&v)[4]) {
-        const f32x4 q = reinterpret_cast<const f32x4 *>(base)[i];
+        const vec q = reinterpret_cast<const vec *>(base)[i];
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
     __device__ static void store_nt(T *row, int i, const float (&v)[4]) {
-        const f32x4 q = {v[0], v[1], v[2], v[3]};
-        __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(row) + i);
+        const vec q = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<vec *>(row) + i);
     }
-};
-
-template <>
-struct Access<ST_F32, 1> {
-    using T = float;
-    __device__ static void load_nt(const T *row, int i, float (&v)[1]) {
-        v[0] = __builtin_nontemporal_load(row + i);
+    __device__ static float load1_nt(const T *row, int j) {
+        return __builtin_nontemporal_load(row + j);
     }
-    __device__ static void load(const T *base, int i, float (&v)[1]) {
-        v[0] = base[i];
-    }
-    __device__ static void store_nt(T *row, int i, const float (&v)[1]) {
-        __builtin_nontemporal_store(v[0], row + i);
+    __device__ static float load1(const T *base, int j) { return base[j]; }
+    __device__ static void store1_nt(T *row, int j, float v) {
+        __builtin_nontemporal_store(v, row + j);
     }
 };
 
 // bf16 -> f32 is exact (a bf16 is the upper half of an f32); f32 -> bf16
 // rounds to nearest even (gfx950's v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(unsigned int w) {
     return __uint_as_float(w << 16);
 }
@@ -98,42 +95,38 @@ __device__ __forceinline__ unsigned int bf16_pack(float lo, float hi) {
 }
 
 template <>
-struct Access<ST_BF16, 8> {
+struct Codec<ST_BF16> {
     using T = unsigned short;
-    __device__ static void unpack(const u32x4 q, float (&v)[8]) {
+    static constexpr int W = 8;
+    typedef unsigned int vec __attribute__((ext_vector_type(4), aligned(2)));
+    __device__ static void unpack(const vec q, float (&v)[8]) {
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
         v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
         v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
     __device__ static void load_nt(const T *row, int i, float (&v)[8]) {
-        unpack(__builtin_nontemporal_load(
-                   reinterpret_cast<const u32x4 *>(row) + i), v);
+        unpack(__builtin_nontemporal_load(reinterpret_cast<const vec *>(row) + i),
+               v);
     }
     __device__ static void load(const T *base, int i, float (&v)[8]) {
-        unpack(reinterpret_cast<const u32x4 *>(base)[i], v);
+        unpack(reinterpret_cast<const vec *>(base)[i], v);
     }
     __device__ static void store_nt(T *row, int i, const float (&v)[8]) {
-        const u32x4 q = {bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3]),
-                         bf16_pack(v[4], v[5]), bf16_pack(v[6], v[7])};
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(row) + i);
+        const vec q = {bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3]),
+                       bf16_pack(v[4], v[5]), bf16_pack(v[6], v[7])};
+        __builtin_nontemporal_store(q, reinterpret_cast<vec *>(row) + i);
     }
-};
-
-template <>
-struct Access<ST_BF16, 1> {
-    using T = unsigned short;
-    __device__ static void load_nt(const T *row, int i, float (&v)[1]) {
-        v[0] = __uint_as_float(
-            (unsigned int)__builtin_nontemporal_load(row + i) << 16);
+    __device__ static float load1_nt(const T *row, int j) {
+        return __uint_as_float((unsigned int)__builtin_nontemporal_load(row + j)
+                               << 16);
     }
-    __device__ static void load(const T *base, int i, float (&v)[1]) {
-        v[0] = __uint_as_float((unsigned int)base[i] << 16);
+    __device__ static float load1(const T *base, int j) {
+        return __uint_as_float((unsigned int)base[j] << 16);
     }
-    __device__ static void store_nt(T *row, int i, const float (&v)[1]) {
-        const unsigned short b =
-            __builtin_bit_cast(unsigned short, (__bf16)v[0]);
-        __builtin_nontemporal_store(b, row + i);
+    __device__ static void store1_nt(T *row, int j, float v) {
+        __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, (__bf16)v),
+                                    row + j);
     }
 };
 
@@ -214,102 +207,185 @@ __device__ __forceinline__ void zero(float (&v)[W]) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-tile kernel
+// One row (or one chunk of a row), shared by both kernels.
+//
+// The lane holds vectors vbase + k*vstride (k < VPT) of the row and, when
+// `sown`, the remainder elements sbase + q*sstride (q < EX) that follow the
+// last whole vector. `reduce(s, which)` turns this lane's partial sum of
+// squares into the row total (which = 0 for the first norm, 1 for the
+// second); every lane of the row must call it.
+//
+// Plain:  y = x * (1/sqrt(sum/n + eps0)) * g0
+// Tail:   h = r + a * (1/sqrt(sum_a/n + eps0)) * g0;  y = h * (1/sqrt(sum_h/n
+//         + eps1)) * g1, with h kept in registers between the two norms.
+// LATE (tail only) loads r while forming h instead of with a.
 // ---------------------------------------------------------------------------
-template <int G>
-constexpr int rowtile_block() { return G >= 128 ? G : 256; }
-
-template <int OP, int ST, int W, int G, int VPT>
-__global__ void __launch_bounds__(rowtile_block<G>())
-rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
-    using A = Access<ST, W>;
-    using T = typename A::T;
-    constexpr int BLOCK = rowtile_block<G>();
-    constexpr int RPB = BLOCK / G;
-    constexpr int WPR = G > 64 ? G / 64 : 1;
-    __shared__ float red[2][WPR];
-
-    const int tid = threadIdx.x;
-    const int sub = tid & (G - 1);
-    const int64_t row = row0 + (int64_t)blockIdx.x * RPB + tid / G;
-    const bool live = row < row_end;
-    const int64_t off = live ? row * (int64_t)p.n : 0;
+template <int OP, int ST, int VPT, int EX, bool LATE, class Reduce>
+__device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
+                                            bool live, int vbase, int vstride,
+                                            int sbase, int sstride, bool sown,
+                                            Reduce reduce) {
+    using C = Codec<ST>;
+    using T = typename C::T;
+    constexpr int W = C::W;
+    constexpr bool HOLD_R = OP == OP_TAIL && !LATE;
     const int nv = p.nv;
+    const int rem = p.rem;
+    const int tail0 = nv * W;  // first remainder element of the row
 
-    float v0[VPT][W];
-    float v1[OP == OP_TAIL ? VPT : 1][W];
+    float v0[VPT][W], e0[EX];
+    float v1[HOLD_R ? VPT : 1][W], e1[HOLD_R ? EX : 1];
     (void)v1;
+    (void)e1;
 
     const T *x0 = static_cast<const T *>(p.x0) + off;
+    const T *x1 = static_cast<const T *>(p.x1) + off;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int i = k * G + sub;
-        if (live && i < nv) A::load_nt(x0, i, v0[k]); else zero(v0[k]);
+        const int i = vbase + k * vstride;
+        if (live && i < nv) C::load_nt(x0, i, v0[k]); else zero(v0[k]);
     }
-    if constexpr (OP == OP_TAIL) {
-        const T *x1 = static_cast<const T *>(p.x1) + off;
+#pragma unroll
+    for (int q = 0; q < EX; ++q) {
+        const int j = sbase + q * sstride;
+        e0[q] = (live && sown && j < rem) ? C::load1_nt(x0, tail0 + j) : 0.0f;
+    }
+    if constexpr (HOLD_R) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int i = k * G + sub;
-            if (live && i < nv) A::load_nt(x1, i, v1[k]); else zero(v1[k]);
+            const int i = vbase + k * vstride;
+            if (live && i < nv) C::load_nt(x1, i, v1[k]); else zero(v1[k]);
+        }
+#pragma unroll
+        for (int q = 0; q < EX; ++q) {
+            const int j = sbase + q * sstride;
+            e1[q] = (live && sown && j < rem) ? C::load1_nt(x1, tail0 + j)
+                                              : 0.0f;
         }
     }
 
     float s = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) s += sumsq<W>(v0[k]);
-    const float inv0 = inv_rms(row_total<G>(s, red[0]), p.n, p.eps0);
+#pragma unroll
+    for (int q = 0; q < EX; ++q) s = fmaf(e0[q], e0[q], s);
+    const float inv0 = inv_rms(reduce(s, 0), p.n, p.eps0);
 
     const T *g0 = static_cast<const T *>(p.g0);
     T *out0 = static_cast<T *>(p.out0) + off;
     if constexpr (OP == OP_PLAIN) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int i = k * G + sub;
+            const int i = vbase + k * vstride;
             if (live && i < nv) {
                 float g[W], o[W];
-                A::load(g0, i, g);
+                C::load(g0, i, g);
 #pragma unroll
                 for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
-                A::store_nt(out0, i, o);
+                C::store_nt(out0, i, o);
             }
         }
+#pragma unroll
+        for (int q = 0; q < EX; ++q) {
+            const int j = sbase + q * sstride;
+            if (live && sown && j < rem)
+                C::store1_nt(out0, tail0 + j,
+                             e0[q] * inv0 * C::load1(g0, tail0 + j));
+        }
     } else {
-        // h = r + a * inv_a * gamma_post, kept in v1 for the second norm.
+        // h lives in v1/e1, or in v0/e0 once a is consumed when r is late.
+        float(*hv)[W] = LATE ? v0 : v1;
+        float *he = LATE ? e0 : e1;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int i = k * G + sub;
+            const int i = vbase + k * vstride;
             if (live && i < nv) {
-                float g[W];
-                A::load(g0, i, g);
+                float g[W], rr[W];
+                C::load(g0, i, g);
+                if constexpr (LATE) {
+                    C::load_nt(x1, i, rr);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < W; ++e) rr[e] = v1[k][e];
+                }
 #pragma unroll
                 for (int e = 0; e < W; ++e)
-                    v1[k][e] = fmaf(v0[k][e] * inv0, g[e], v1[k][e]);
-                A::store_nt(out0, i, v1[k]);
+                    hv[k][e] = fmaf(v0[k][e] * inv0, g[e], rr[e]);
+                C::store_nt(out0, i, hv[k]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EX; ++q) {
+            const int j = sbase + q * sstride;
+            if (live && sown && j < rem) {
+                const float rr = LATE ? C::load1_nt(x1, tail0 + j) : e1[q];
+                he[q] = fmaf(e0[q] * inv0, C::load1(g0, tail0 + j), rr);
+                C::store1_nt(out0, tail0 + j, he[q]);
             }
         }
         float sh = 0.0f;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) sh += sumsq<W>(v1[k]);
-        const float inv1 = inv_rms(row_total<G>(sh, red[1]), p.n, p.eps1);
+        for (int k = 0; k < VPT; ++k) sh += sumsq<W>(hv[k]);
+#pragma unroll
+        for (int q = 0; q < EX; ++q) sh = fmaf(he[q], he[q], sh);
+        const float inv1 = inv_rms(reduce(sh, 1), p.n, p.eps1);
+
         const T *g1 = static_cast<const T *>(p.g1);
         T *out1 = static_cast<T *>(p.out1) + off;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int i = k * G + sub;
+            const int i = vbase + k * vstride;
             if (live && i < nv) {
                 float g[W], o[W];
-                A::load(g1, i, g);
+                C::load(g1, i, g);
 #pragma unroll
-                for (int e = 0; e < W; ++e) o[e] = v1[k][e] * inv1 * g[e];
-                A::store_nt(out1, i, o);
+                for (int e = 0; e < W; ++e) o[e] = hv[k][e] * inv1 * g[e];
+                C::store_nt(out1, i, o);
             }
+        }
+#pragma unroll
+        for (int q = 0; q < EX; ++q) {
+            const int j = sbase + q * sstride;
+            if (live && sown && j < rem)
+                C::store1_nt(out1, tail0 + j,
+                             he[q] * inv1 * C::load1(g1, tail0 + j));
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Split-row kernel
+// Row-tile kernel: G lanes per row, VPT vectors per lane. G <= 64 packs
+// 64/G rows into each wavefront; G > 64 is one row per workgroup.
+// ---------------------------------------------------------------------------
+template <int G>
+constexpr int rowtile_block() { return G >= 128 ? G : 256; }
+
+// Remainder elements each lane may hold: a row has at most W - 1 of them.
+template <int ST, int G>
+constexpr int rowtile_extra() {
+    return (Codec<ST>::W - 1 + G - 1) / G;
+}
+
+template <int OP, int ST, int G, int VPT, bool LATE = false>
+__global__ void __launch_bounds__(rowtile_block<G>())
+rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
+    constexpr int BLOCK = rowtile_block<G>();
+    constexpr int RPB = BLOCK / G;
+    constexpr int WPR = G > 64 ? G / 64 : 1;
+    __shared__ float red[2][WPR];
+
+    const int sub = threadIdx.x & (G - 1);
+    const int64_t row = row0 + (int64_t)blockIdx.x * RPB + threadIdx.x / G;
+    const bool live = row < row_end;
+    const int64_t off = live ? row * (int64_t)p.n : 0;
+    process_row<OP, ST, VPT, rowtile_extra<ST, G>(), LATE>(
+        p, off, live, sub, G, sub, G, true,
+        [&](float s, int which) { return row_total<G>(s, red[which]); });
+}
+
+// ---------------------------------------------------------------------------
+// Split-row kernel: chunk c of rows g, g + groups, ... for workgroup
+// (g, c) of a cooperative grid of groups x chunks workgroups.
 // ---------------------------------------------------------------------------
 constexpr int SB = kSplitBlock;
 constexpr int SNW = SB / 64;
@@ -328,7 +404,8 @@ __device__ __forceinline__ float block_total(float s, float *slot) {
 // Publish this chunk's partial, gather the partials of every chunk of the
 // row in chunk order, and leave the row's slots at zero once every chunk has
 // read them. `set` selects one of two independent slot sets (the tail's two
-// reductions).
+// reductions). Each slot is one 64-bit word (flag in the high half, the f32
+// partial in the low half), so no fence is needed between value and flag.
 __device__ float cross_chunk_total(float partial, const SplitState &st,
                                    int set, int64_t row_local, int chunk,
                                    int chunks, float *part) {
@@ -373,96 +450,29 @@ __device__ float cross_chunk_total(float partial, const SplitState &st,
     return t;
 }
 
-template <int OP, int ST, int W, int VPT>
+template <int OP, int ST, int VPT>
 __global__ void __launch_bounds__(SB)
 split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
              int chunks, int groups) {
-    using A = Access<ST, W>;
-    using T = typename A::T;
     __shared__ float red[2][SNW];
     __shared__ float part[kSplitMaxChunks];
 
     const int tid = threadIdx.x;
     const int chunk = (int)(blockIdx.x % (unsigned)chunks);
     const int group = (int)(blockIdx.x / (unsigned)chunks);
-    const int first = chunk * (SB * VPT) + tid;
-    const int nv = p.nv;
-    const T *g0 = static_cast<const T *>(p.g0);
-    const T *g1 = static_cast<const T *>(p.g1);
+    const int vbase = chunk * (SB * VPT) + tid;
+    const bool last = chunk == chunks - 1;  // the last chunk owns the remainder
 
     for (int64_t rl = group; rl < nrows; rl += groups) {
         const int64_t off = (row0 + rl) * (int64_t)p.n;
-        float v0[VPT][W];
-        float v1[OP == OP_TAIL ? VPT : 1][W];
-        (void)v1;
-        const T *x0 = static_cast<const T *>(p.x0) + off;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = first + k * SB;
-            if (i < nv) A::load_nt(x0, i, v0[k]); else zero(v0[k]);
-        }
-        if constexpr (OP == OP_TAIL) {
-            const T *x1 = static_cast<const T *>(p.x1) + off;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int i = first + k * SB;
-                if (i < nv) A::load_nt(x1, i, v1[k]); else zero(v1[k]);
-            }
-        }
-        float s = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) s += sumsq<W>(v0[k]);
-        const float tot0 = cross_chunk_total(block_total(s, red[0]), st, 0, rl,
-                                             chunk, chunks, part);
-        const float inv0 = inv_rms(tot0, p.n, p.eps0);
-
-        T *out0 = static_cast<T *>(p.out0) + off;
-        if constexpr (OP == OP_PLAIN) {
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int i = first + k * SB;
-                if (i < nv) {
-                    float g[W], o[W];
-                    A::load(g0, i, g);
-#pragma unroll
-                    for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
-                    A::store_nt(out0, i, o);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int i = first + k * SB;
-                if (i < nv) {
-                    float g[W];
-                    A::load(g0, i, g);
-#pragma unroll
-                    for (int e = 0; e < W; ++e)
-                        v1[k][e] = fmaf(v0[k][e] * inv0, g[e], v1[k][e]);
-                    A::store_nt(out0, i, v1[k]);
-                }
-            }
-            float sh = 0.0f;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) sh += sumsq<W>(v1[k]);
-            const float tot1 = cross_chunk_total(block_total(sh, red[1]), st,
-                                                 1, rl, chunk, chunks, part);
-            const float inv1 = inv_rms(tot1, p.n, p.eps1);
-            T *out1 = static_cast<T *>(p.out1) + off;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int i = first + k * SB;
-                if (i < nv) {
-                    float g[W], o[W];
-                    A::load(g1, i, g);
-#pragma unroll
-                    for (int e = 0; e < W; ++e) o[e] = v1[k][e] * inv1 * g[e];
-                    A::store_nt(out1, i, o);
-                }
-            }
-        }
-        // The next row reuses `part` and `red`: every lane must have finished
-        // reading them (cross_chunk_total's sums) before they are rewritten.
+        process_row<OP, ST, VPT, 1, false>(
+            p, off, true, vbase, SB, tid, SB, last,
+            [&](float s, int which) {
+                return cross_chunk_total(block_total(s, red[which]), st, which,
+                                         rl, chunk, chunks, part);
+            });
+        // The next row rewrites `part` and `red`: every lane must have
+        // finished reading them first.
         __syncthreads();
     }
 }
@@ -477,26 +487,26 @@ __global__ void zero_kernel(unsigned int *p, int64_t words) {
 // ---------------------------------------------------------------------------
 // Launchers and the kernel table
 // ---------------------------------------------------------------------------
-template <int OP, int ST, int W, int G, int VPT>
+template <int OP, int ST, int G, int VPT, bool LATE = false>
 hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
                           hipStream_t stream) {
     constexpr int BLOCK = rowtile_block<G>();
     constexpr int RPB = BLOCK / G;
     const int64_t blocks = (nrows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((rowtile_kernel<OP, ST, W, G, VPT>),
+    hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT, LATE>),
                        dim3((unsigned int)blocks), dim3(BLOCK), 0, stream, p,
                        row0, row0 + nrows);
     return hipGetLastError();
 }
 
-template <int OP, int ST, int W, int G, int VPT>
+template <int OP, int ST, int G, int VPT, bool LATE = false>
 hipError_t occupancy_rowtile(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, rowtile_kernel<OP, ST, W, G, VPT>, rowtile_block<G>(),
-        0);
+        blocks_per_cu, rowtile_kernel<OP, ST, G, VPT, LATE>,
+        rowtile_block<G>(), 0);
 }
 
-template <int OP, int ST, int W, int VPT>
+template <int OP, int ST, int VPT>
 hipError_t launch_split(const RowArgs &p, const SplitState &st, int64_t row0,
                         int64_t nrows, int chunks, int groups,
                         hipStream_t stream) {
@@ -505,50 +515,48 @@ hipError_t launch_split(const RowArgs &p, const SplitState &st, int64_t row0,
     int c = chunks, g = groups;
     void *args[] = {&pa, &sa, &row0, &nrows, &c, &g};
     return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&split_kernel<OP, ST, W, VPT>),
+        reinterpret_cast<const void *>(&split_kernel<OP, ST, VPT>),
         dim3((unsigned int)(groups * chunks)), dim3(SB), args, 0, stream);
 }
 
-template <int OP, int ST, int W, int VPT>
+template <int OP, int ST, int VPT>
 hipError_t occupancy_split(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, split_kernel<OP, ST, W, VPT>, SB, 0);
+        blocks_per_cu, split_kernel<OP, ST, VPT>, SB, 0);
 }
 
-#define SNR_RT(OP, ST, W, G, VPT)                                         \
-    KernelEntry{OP, ST, W, KIND_ROWTILE, G, VPT, rowtile_block<G>(),      \
-                &launch_rowtile<OP, ST, W, G, VPT>, nullptr,              \
-                &occupancy_rowtile<OP, ST, W, G, VPT>}
-#define SNR_SPLIT(OP, ST, W, VPT)                                         \
-    KernelEntry{OP, ST, W, KIND_SPLIT, SB, VPT, SB, nullptr,              \
-                &launch_split<OP, ST, W, VPT>, &occupancy_split<OP, ST, W, VPT>}
+#define SNR_RT(OP, ST, G, VPT)                                              \
+    KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
+                rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
+                nullptr, &occupancy_rowtile<OP, ST, G, VPT>}
+#define SNR_RT_LATE(G, VPT)                                                 \
+    KernelEntry{OP_TAIL, ST_F32, 4, KIND_ROWTILE, G, VPT, rowtile_block<G>(), \
+                &launch_rowtile<OP_TAIL, ST_F32, G, VPT, true>, nullptr,    \
+                &occupancy_rowtile<OP_TAIL, ST_F32, G, VPT, true>}
+#define SNR_SPLIT(OP, ST, VPT)                                              \
+    KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, VPT, SB, nullptr,      \
+                &launch_split<OP, ST, VPT>, &occupancy_split<OP, ST, VPT>}
 
-// The shapes compiled for one (operation, storage, load width). Sub-wavefront
-// groups hold 4 loads per lane; whole wavefronts and workgroups hold up to 16.
-#define SNR_SHAPES(OP, ST, W)                                              \
-    SNR_RT(OP, ST, W, 1, 4), SNR_RT(OP, ST, W, 2, 4),                      \
-    SNR_RT(OP, ST, W, 4, 4), SNR_RT(OP, ST, W, 8, 4),                      \
-    SNR_RT(OP, ST, W, 16, 4), SNR_RT(OP, ST, W, 32, 4),                    \
-    SNR_RT(OP, ST, W, 64, 2), SNR_RT(OP, ST, W, 64, 4),                    \
-    SNR_RT(OP, ST, W, 64, 8), SNR_RT(OP, ST, W, 64, 16),                   \
-    SNR_RT(OP, ST, W, 128, 8), SNR_RT(OP, ST, W, 128, 13),                 \
-    SNR_RT(OP, ST, W, 128, 16), SNR_RT(OP, ST, W, 256, 4),                 \
-    SNR_RT(OP, ST, W, 256, 7), SNR_RT(OP, ST, W, 256, 8),                  \
-    SNR_RT(OP, ST, W, 256, 16), SNR_RT(OP, ST, W, 512, 4),                 \
-    SNR_RT(OP, ST, W, 512, 8), SNR_RT(OP, ST, W, 512, 16),                 \
-    SNR_RT(OP, ST, W, 1024, 2), SNR_RT(OP, ST, W, 1024, 4),                \
-    SNR_RT(OP, ST, W, 1024, 8), SNR_SPLIT(OP, ST, W, 8)
+// The shapes compiled for one (operation, storage). Sub-wavefront groups
+// hold 4 vectors per lane; whole wavefronts and workgroups hold up to 16.
+#define SNR_SHAPES(OP, ST)                                                  \
+    SNR_RT(OP, ST, 1, 4), SNR_RT(OP, ST, 2, 4), SNR_RT(OP, ST, 4, 4),       \
+    SNR_RT(OP, ST, 8, 4), SNR_RT(OP, ST, 16, 4), SNR_RT(OP, ST, 32, 4),     \
+    SNR_RT(OP, ST, 64, 2), SNR_RT(OP, ST, 64, 4), SNR_RT(OP, ST, 64, 8),    \
+    SNR_RT(OP, ST, 64, 16), SNR_RT(OP, ST, 128, 8), SNR_RT(OP, ST, 128, 13), \
+    SNR_RT(OP, ST, 128, 16), SNR_RT(OP, ST, 256, 4), SNR_RT(OP, ST, 256, 7), \
+    SNR_RT(OP, ST, 256, 8), SNR_RT(OP, ST, 256, 16), SNR_RT(OP, ST, 512, 4), \
+    SNR_RT(OP, ST, 512, 8), SNR_RT(OP, ST, 512, 16),                        \
+    SNR_RT(OP, ST, 1024, 2), SNR_RT(OP, ST, 1024, 4),                       \
+    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST, 8)
 
-// 1024 lanes x 16 loads only where the row fits in the 128 registers a lane
-// of a 1024-lane workgroup may use (it spills for 8-wide bf16 and the tail's
-// two 4-wide streams).
+// 1024 lanes x 16 vectors only where the row fits in the 128 registers a
+// lane of a 1024-lane workgroup may use: not for 8-wide bf16, and for the
+// tail only with r loaded late (a/h resident, not a and r).
 const KernelEntry kTable[] = {
-    SNR_SHAPES(OP_PLAIN, ST_F32, 4),  SNR_RT(OP_PLAIN, ST_F32, 4, 1024, 16),
-    SNR_SHAPES(OP_PLAIN, ST_F32, 1),  SNR_RT(OP_PLAIN, ST_F32, 1, 1024, 16),
-    SNR_SHAPES(OP_PLAIN, ST_BF16, 8),
-    SNR_SHAPES(OP_PLAIN, ST_BF16, 1), SNR_RT(OP_PLAIN, ST_BF16, 1, 1024, 16),
-    SNR_SHAPES(OP_TAIL, ST_F32, 4),
-    SNR_SHAPES(OP_TAIL, ST_F32, 1),   SNR_RT(OP_TAIL, ST_F32, 1, 1024, 16),
+    SNR_SHAPES(OP_PLAIN, ST_F32), SNR_RT(OP_PLAIN, ST_F32, 1024, 16),
+    SNR_SHAPES(OP_PLAIN, ST_BF16),
+    SNR_SHAPES(OP_TAIL, ST_F32),  SNR_RT_LATE(1024, 16),
 };
 
 }  // namespace

@@ -21,15 +21,15 @@ from parity import (TOL_BF16, TOL_F32, bf16_as_f64, plain_error,  # noqa: E402
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-# Row-tile shapes compiled for every (operation, storage, width); 1024 x 16
-# exists only where the row fits the registers of a 1024-lane workgroup.
+# Row-tile shapes compiled for every (operation, storage); 1024 x 16 exists
+# only where the row fits the registers of a 1024-lane workgroup.
 ROWTILE_SHAPES = [(1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (32, 4),
                   (64, 2), (64, 4), (64, 8), (64, 16), (128, 8), (128, 13),
                   (128, 16), (256, 4), (256, 7), (256, 8), (256, 16),
                   (512, 4), (512, 8), (512, 16), (1024, 2), (1024, 4),
                   (1024, 8)]
-WIDE_EXTRA = {("plain", "f32", 4), ("plain", "f32", 1), ("plain", "bf16", 1),
-              ("tail", "f32", 1)}
+WIDE_EXTRA = {("plain", "f32"), ("tail", "f32")}
+VEC = {"f32": 4, "bf16": 8}   # elements per 128-bit vector
 
 
 def say(msg):
@@ -110,33 +110,31 @@ def test_config_full_size(oracle, name):
 # ---------------------------------------------------------------------------
 def _shape_cases():
     cases = []
-    for op in ("plain", "tail"):
-        combos = [("f32", 4), ("f32", 1)]
-        if op == "plain":
-            combos += [("bf16", 8), ("bf16", 1)]
-        for st, w in combos:
-            shapes = list(ROWTILE_SHAPES)
-            if (op, st, w) in WIDE_EXTRA:
-                shapes.append((1024, 16))
-            for g, vpt in shapes:
-                cases.append((op, st, w, g, vpt))
+    for op, st in (("plain", "f32"), ("plain", "bf16"), ("tail", "f32")):
+        shapes = list(ROWTILE_SHAPES)
+        if (op, st) in WIDE_EXTRA:
+            shapes.append((1024, 16))
+        for g, vpt in shapes:
+            for ragged in (False, True):
+                cases.append((op, st, g, vpt, ragged))
     return cases
 
 
 def _case_id(c):
-    return "{}-{}-w{}-g{}-v{}".format(*c)
+    return "{}-{}-g{}-v{}-{}".format(*c[:4], "ragged" if c[4] else "whole")
 
 
 @pytest.mark.parametrize("case", _shape_cases(), ids=_case_id)
 def test_forced_rowtile_shape(oracle, case):
-    op, st, w, g, vpt = case
-    cap = g * vpt
-    nv = max(1, cap - g // 2 - (1 if g == 1 else 0))   # ragged in the tile
-    n = nv * w
-    while w == 1 and n % 4 == 0:   # keep rows off the 128-bit path
-        n -= 1
+    """Every compiled shape on a row that leaves part of its tile empty; the
+    ragged variant adds the largest remainder (W - 1 elements past the last
+    whole vector)."""
+    op, st, g, vpt, ragged = case
+    w = VEC[st]
+    nv = max(1, g * vpt - g // 2 - (1 if g == 1 else 0))
+    n = nv * w + (w - 1 if ragged else 0)
     rows = 37
-    seed = 1000 + g * 31 + vpt
+    seed = 1000 + g * 31 + vpt + (7 if ragged else 0)
     say(f"forced rowtile {_case_id(case)} rows={rows} n={n}")
     with snr.forced_shape("rowtile", g, vpt):
         if op == "plain":
@@ -153,27 +151,48 @@ def test_forced_rowtile_shape(oracle, case):
 
 
 @pytest.mark.parametrize("op", ["plain", "tail"])
-@pytest.mark.parametrize("w", [4, 1])
-@pytest.mark.parametrize("chunks_nv", [(1, 100), (3, 2 * 2048 + 5),
+@pytest.mark.parametrize("ragged", [False, True])
+@pytest.mark.parametrize("chunks_nv", [(1, 0), (1, 100), (3, 2 * 2048 + 5),
                                        (5, 5 * 2048)])
-def test_forced_split(oracle, op, w, chunks_nv):
+def test_forced_split(oracle, op, ragged, chunks_nv):
     chunks, nv = chunks_nv
-    # element-wide rows: a width that is not a multiple of 4
-    n = nv * 4 if w == 4 else (nv if nv % 4 else nv - 1)
+    n = nv * 4 + (3 if ragged else 0)
+    if n == 0:
+        n = 1
     rows = 7
-    say(f"forced split op={op} w={w} chunks={chunks} rows={rows} n={n}")
+    say(f"forced split op={op} ragged={ragged} chunks={chunks} rows={rows} "
+        f"n={n}")
     with snr.forced_shape("split", 0, 8):
         if op == "plain":
-            inp = gen.random_plain(rows, n, 77 + chunks)
+            inp = gen.random_plain(rows, n, 77 + chunks + n)
             got, _ = run_plain(inp)
             shape = snr.last_shape()
-            check_plain(oracle, inp, got, f"split-{op}-w{w}-c{chunks}")
+            check_plain(oracle, inp, got, f"split-{op}-n{n}")
         else:
-            inp = gen.random_tail(rows, n, 78 + chunks)
+            inp = gen.random_tail(rows, n, 78 + chunks + n)
             h, y = run_tail(inp)
             shape = snr.last_shape()
-            check_tail(oracle, inp, h, y, f"split-{op}-w{w}-c{chunks}")
-    assert shape == f"split:256:8:{w}:{chunks}", shape
+            check_tail(oracle, inp, h, y, f"split-{op}-n{n}")
+    assert shape == f"split:256:8:4:{chunks}", shape
+    assert snr.split_timeouts() == 0
+
+
+@pytest.mark.parametrize("name", ["edge_256x65536_f32", "edge_256x16384_f32"])
+def test_split_full_size(oracle, name):
+    """The split-row reduction on the edge sweep's widest rows at full size
+    (the automatic choice there is a 1024-lane register tile)."""
+    cfg = gen.CONFIGS[name]
+    say(f"split full size {name}")
+    inp = gen.make(cfg)
+    with snr.forced_shape("split", 0, 8):
+        got, _ = run_plain(inp)
+        shape = snr.last_shape()
+    check_plain(oracle, inp, got, f"split-{name}")
+    assert shape.startswith("split:256:8:4:")
+    tin = gen.random_tail(64, cfg.n, 9100 + cfg.n)
+    with snr.forced_shape("split", 0, 8):
+        h, y = run_tail(tin)
+    check_tail(oracle, tin, h, y, f"split-tail-{cfg.n}")
     assert snr.split_timeouts() == 0
 
 
@@ -219,8 +238,8 @@ def test_ragged_tail(oracle, n):
 
 @pytest.mark.parametrize("n", [6656, 768, 4096])
 def test_misaligned_base_pointer(oracle, n):
-    """A view one element into its allocation is not 16-byte aligned: the
-    element-wide path must run and agree."""
+    """A view one element into its allocation is not 16-byte aligned: rows
+    still move with 128-bit accesses and give the aligned result exactly."""
     rows = 16
     say(f"misaligned rows={rows} n={n}")
     inp = gen.random_plain(rows, n, 6000 + n)
@@ -234,12 +253,12 @@ def test_misaligned_base_pointer(oracle, n):
     y = ybuf[1:].view(rows, n)
     snr.rmsnorm_fwd(x, g, inp["eps"], out=y)
     torch.cuda.synchronize()
-    assert snr.last_shape().endswith(":1"), snr.last_shape()
-    check_plain(oracle, inp, host_f64(y), f"misaligned-{n}")
-    # the same rows from an aligned allocation take the 128-bit path
+    misaligned = host_f64(y)
+    assert snr.last_shape().endswith(":4"), snr.last_shape()
+    check_plain(oracle, inp, misaligned, f"misaligned-{n}")
+    # the same rows from an aligned allocation give the same bits
     got, _ = run_plain(inp)
-    assert snr.last_shape().endswith(":4")
-    check_plain(oracle, inp, got, f"aligned-{n}")
+    assert np.array_equal(got, misaligned)
 
 
 # ---------------------------------------------------------------------------
@@ -329,3 +348,22 @@ def test_bf16_output_is_round_to_nearest_even(oracle):
     # same sign everywhere (the sign bit would make the difference huge)
     assert ulps.max() <= 1, ulps.max()
     assert np.mean(ulps == 0) >= 0.999, np.mean(ulps == 0)
+
+
+def test_split_wait_budget_exhausted_is_reported_and_recovered(oracle,
+                                                              monkeypatch):
+    """Force the split-row kernel's bounded wait to give up (a budget of one
+    poll): the kernel still finishes, the overrun is counted, and the next
+    call with the normal budget is correct again."""
+    rows, n = 64, 5 * 2048 * 4
+    say(f"split watchdog rows={rows} n={n}")
+    inp = gen.random_plain(rows, n, 4242)
+    assert snr.split_timeouts() == 0
+    monkeypatch.setenv("SNR_SPLIT_SPIN_LIMIT", "1")
+    with snr.forced_shape("split", 0, 8):
+        run_plain(inp)
+        assert snr.split_timeouts() > 0
+        monkeypatch.delenv("SNR_SPLIT_SPIN_LIMIT")
+        got, _ = run_plain(inp)
+    assert snr.split_timeouts() == 0
+    check_plain(oracle, inp, got, "split-after-watchdog")
