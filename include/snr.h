@@ -56,9 +56,9 @@ enum {
     SNR_ERR_EPS = 4,       /* an epsilon is not finite or not > 0 */
     SNR_ERR_ALIAS = 5,     /* buffers overlap other than in an allowed way */
     SNR_ERR_ALIGN = 6,     /* a pointer is not aligned to its element size */
-    SNR_ERR_WORKSPACE = 7, /* the split-row workspace could not be set up,
-                              or the row is too wide for co-resident
-                              workgroups */
+    SNR_ERR_WORKSPACE = 7, /* the per-stream workspace could not be
+                              allocated, or a forced split shape cannot
+                              keep every chunk of a row co-resident */
     SNR_ERR_HIP = 8,       /* a HIP runtime call failed; see
                               snr_last_hip_error() */
     SNR_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
@@ -144,17 +144,29 @@ SNR_API int snr_last_hip_error(void);
  *                             wavefront, g > 64 spans g/64 wavefronts joined
  *                             by one LDS step
  *          SNR_SHAPE_SPLIT    the row is cut into chunks of 256 x `vpt`
- *                             loads, one workgroup per chunk, joined by a
- *                             two-phase cross-workgroup reduction
+ *                             vectors, one workgroup per chunk, joined by a
+ *                             two-phase cross-workgroup reduction; every
+ *                             chunk of a row must be co-resident
+ *          SNR_SHAPE_MULTIPASS rows wider than that: per-chunk partial sums,
+ *                             a per-row combine and an apply pass through
+ *                             device memory (reads the row twice; the tail
+ *                             also re-reads h). Chosen automatically only
+ *                             when the split shape cannot hold the row.
  * snr_force_shape applies to subsequent calls on the calling thread until it
  * is called again with SNR_SHAPE_AUTO. A forced shape that cannot hold the
  * row (g * vpt loads < row length) or that has no compiled kernel returns
  * SNR_ERR_SHAPE from the call. snr_last_shape writes "rowtile:g:vpt:width"
- * or "split:256:vpt:width:chunks" (width = elements per 128-bit vector) of
+ * or "split:256:vpt:width:chunks" or "multipass:256:8:width:chunks" (width =
+ * elements per 128-bit vector) of
  * the calling thread's most recent successful launch into buf
  * (NUL-terminated).
  */
-enum { SNR_SHAPE_AUTO = 0, SNR_SHAPE_ROWTILE = 1, SNR_SHAPE_SPLIT = 2 };
+enum {
+    SNR_SHAPE_AUTO = 0,
+    SNR_SHAPE_ROWTILE = 1,
+    SNR_SHAPE_SPLIT = 2,
+    SNR_SHAPE_MULTIPASS = 3
+};
 SNR_API int snr_force_shape(int kind, int g, int vpt);
 SNR_API int snr_last_shape(char *buf, int len);
 

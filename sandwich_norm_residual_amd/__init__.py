@@ -116,10 +116,10 @@ def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
 
 @contextlib.contextmanager
 def forced_shape(kind: str, g: int = 0, vpt: int = 0):
-    """Force a dispatch shape ("rowtile" or "split") for calls made on this
-    thread inside the block (diagnostics and tests)."""
+    """Force a dispatch shape ("rowtile", "split" or "multipass") for calls
+    made on this thread inside the block (diagnostics and tests)."""
     code = {"auto": _lib.SHAPE_AUTO, "rowtile": _lib.SHAPE_ROWTILE,
-            "split": _lib.SHAPE_SPLIT}[kind]
+            "split": _lib.SHAPE_SPLIT, "multipass": _lib.SHAPE_MULTIPASS}[kind]
     _lib.force_shape(code, g, vpt)
     try:
         yield
@@ -128,7 +128,8 @@ def forced_shape(kind: str, g: int = 0, vpt: int = 0):
 
 
 def last_shape() -> str:
-    """"kind:g:vpt:width[:chunks]" of this thread's most recent launch."""
+    """"kind:g:vpt:width[:chunks]" of this thread's most recent launch
+    (width = elements per 128-bit vector)."""
     return _lib.last_shape()
 
 

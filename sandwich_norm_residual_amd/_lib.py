@@ -29,6 +29,7 @@ SNR_ERR_DEVICE = 9
 SHAPE_AUTO = 0
 SHAPE_ROWTILE = 1
 SHAPE_SPLIT = 2
+SHAPE_MULTIPASS = 3
 
 # Every function include/snr.h declares, with its ctypes signature.
 _vp = ctypes.c_void_p

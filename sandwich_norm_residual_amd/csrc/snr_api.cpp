@@ -73,17 +73,19 @@ int current_device(int *dev, DeviceInfo *info) {
 constexpr int64_t kSlotCap = int64_t(1) << 18;  // partial slots per set
 constexpr int64_t kRowCap = int64_t(1) << 18;   // rows per launch
 constexpr uint32_t kSpinLimit = 1u << 22;       // polls before giving up
+constexpr int64_t kMultiFloats = int64_t(1) << 20;  // multi-pass scratch
 
 struct Workspace {
     void *base = nullptr;
     int64_t words = 0;
     SplitState st{};
+    float *multi = nullptr;  // multi-pass partial sums and inverse norms
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(int dev, hipStream_t stream, SplitState *out) {
+int get_workspace(int dev, hipStream_t stream, Workspace *out) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     auto key = std::make_pair(dev, stream);
     auto it = g_ws.find(key);
@@ -91,7 +93,8 @@ int get_workspace(int dev, hipStream_t stream, SplitState *out) {
         Workspace w;
         const int64_t slot_bytes = 2 * kSlotCap * 8;
         const int64_t depart_bytes = 2 * kRowCap * 4;
-        const int64_t bytes = slot_bytes + depart_bytes + 256;
+        const int64_t multi_bytes = kMultiFloats * 4;
+        const int64_t bytes = slot_bytes + depart_bytes + 256 + multi_bytes;
         hipError_t e = hipMalloc(&w.base, (size_t)bytes);
         if (e != hipSuccess) {
             t_last_hip_error = (int)e;
@@ -111,9 +114,11 @@ int get_workspace(int dev, hipStream_t stream, SplitState *out) {
         w.st.slot_cap = kSlotCap;
         w.st.row_cap = kRowCap;
         w.st.spin_limit = kSpinLimit;
+        w.multi = reinterpret_cast<float *>(b + slot_bytes + depart_bytes +
+                                            256);
         it = g_ws.emplace(key, w).first;
     }
-    *out = it->second.st;
+    *out = it->second;
     return SNR_OK;
 }
 
@@ -150,7 +155,7 @@ const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
     const KernelEntry *t = kernel_table(&count);
     for (int i = 0; i < count; ++i)
         if (t[i].op == op && t[i].storage == st && t[i].width == w &&
-            t[i].kind == kind && (kind == KIND_SPLIT || t[i].g == g) &&
+            t[i].kind == kind && (kind != KIND_ROWTILE || t[i].g == g) &&
             t[i].vpt == vpt)
             return &t[i];
     return nullptr;
@@ -170,6 +175,12 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
     }
     if (t_force_kind == SNR_SHAPE_SPLIT) {
         c->k = find_entry(op, st, w, KIND_SPLIT, 0, t_force_vpt);
+        if (!c->k) return SNR_ERR_SHAPE;
+        c->chunks = split_chunks(c->k, nv);
+        return SNR_OK;
+    }
+    if (t_force_kind == SNR_SHAPE_MULTIPASS) {
+        c->k = find_entry(op, st, w, KIND_MULTIPASS, 0, kMultiVpt);
         if (!c->k) return SNR_ERR_SHAPE;
         c->chunks = split_chunks(c->k, nv);
         return SNR_OK;
@@ -228,6 +239,23 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     if (rc != SNR_OK) return rc;
     const KernelEntry *k = c.k;
 
+    if (k->kind == KIND_SPLIT) {
+        // The cooperative grid needs every chunk of a row co-resident; rows
+        // wider than that go through the multi-pass kernels instead (unless
+        // the split shape was forced, which then fails).
+        int per_cu = 0;
+        hipError_t e = k->occupancy(&per_cu);
+        if (e != hipSuccess) return hip_fail(e);
+        const bool fits = c.chunks <= kSplitMaxChunks &&
+                          (int64_t)per_cu * info.cus >= c.chunks;
+        if (!fits) {
+            if (t_force_kind == SNR_SHAPE_SPLIT) return SNR_ERR_WORKSPACE;
+            k = find_entry(op, st, w, KIND_MULTIPASS, 0, kMultiVpt);
+            if (!k) return SNR_ERR_SHAPE;
+            c.chunks = split_chunks(k, a.nv);
+        }
+    }
+
     if (k->kind == KIND_ROWTILE) {
         const int rpb = k->block / k->g;
         const int64_t max_blocks = (int64_t)(UINT32_MAX / (uint32_t)k->block);
@@ -237,8 +265,23 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             hipError_t e = k->rowtile(a, r0, nr, stream);
             if (e != hipSuccess) return hip_fail(e);
         }
+    } else if (k->kind == KIND_MULTIPASS) {
+        Workspace ws;
+        rc = get_workspace(dev, stream, &ws);
+        if (rc != SNR_OK) return rc;
+        // partial sums (rows x chunks) and inverse norms (rows) must fit the
+        // scratch; each pass's grid (rows x chunks workgroups) must fit a
+        // launch
+        int64_t step = kMultiFloats / (c.chunks + 1);
+        const int64_t max_grid = (int64_t)(UINT32_MAX / (uint32_t)k->block);
+        if (step * c.chunks > max_grid) step = max_grid / c.chunks;
+        if (step < 1) return SNR_ERR_SHAPE;
+        for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
+            const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
+            hipError_t e = k->multipass(a, ws.multi, r0, nr, c.chunks, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
     } else {
-        if (c.chunks > kSplitMaxChunks) return SNR_ERR_SHAPE;
         int per_cu = 0;
         hipError_t e = k->occupancy(&per_cu);
         if (e != hipSuccess) return hip_fail(e);
@@ -246,9 +289,10 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         // most floor(capacity / chunks) rows are in flight at once.
         const int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
         if (max_groups < 1) return SNR_ERR_WORKSPACE;
-        SplitState ws;
-        rc = get_workspace(dev, stream, &ws);
+        Workspace w_all;
+        rc = get_workspace(dev, stream, &w_all);
         if (rc != SNR_OK) return rc;
+        SplitState ws = w_all.st;
         // Test hook: a small poll budget forces the bounded-wait path.
         if (const char *lim = std::getenv("SNR_SPLIT_SPIN_LIMIT")) {
             const long v = std::strtol(lim, nullptr, 10);
@@ -267,8 +311,9 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         std::snprintf(t_last_shape, sizeof t_last_shape, "rowtile:%d:%d:%d",
                       k->g, k->vpt, w);
     else
-        std::snprintf(t_last_shape, sizeof t_last_shape, "split:%d:%d:%d:%d",
-                      k->g, k->vpt, w, c.chunks);
+        std::snprintf(t_last_shape, sizeof t_last_shape, "%s:%d:%d:%d:%d",
+                      k->kind == KIND_SPLIT ? "split" : "multipass", k->g,
+                      k->vpt, w, c.chunks);
     if (debug_enabled())
         std::fprintf(stderr, "[snr] %s rows=%lld n=%d -> %s\n",
                      op == OP_TAIL ? "sandwich_tail" : "rmsnorm_fwd",
@@ -372,7 +417,7 @@ int snr_last_hip_error(void) { return t_last_hip_error; }
 
 int snr_force_shape(int kind, int g, int vpt) {
     if (kind != SNR_SHAPE_AUTO && kind != SNR_SHAPE_ROWTILE &&
-        kind != SNR_SHAPE_SPLIT)
+        kind != SNR_SHAPE_SPLIT && kind != SNR_SHAPE_MULTIPASS)
         return SNR_ERR_SHAPE;
     t_force_kind = kind;
     t_force_g = g;

@@ -9,7 +9,7 @@ namespace snr {
 
 enum Op : int { OP_PLAIN = 0, OP_TAIL = 1 };
 enum Storage : int { ST_F32 = 0, ST_BF16 = 1 };
-enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2 };
+enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2, KIND_MULTIPASS = 3 };
 
 // Everything a row kernel needs. For OP_PLAIN only x0, g0, out0 and eps0 are
 // used; for OP_TAIL: x0 = a, x1 = r, g0 = gamma_post, g1 = gamma_pre,
@@ -52,6 +52,13 @@ using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
                                    int64_t row0, int64_t nrows, int chunks,
                                    int groups, hipStream_t);
 using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
+using MultipassLaunch = hipError_t (*)(const RowArgs &, float *scratch,
+                                       int64_t row0, int64_t nrows,
+                                       int chunks, hipStream_t);
+
+// Geometry of the multi-pass kernels: 256 threads x 8 vectors per chunk.
+constexpr int kMultiBlock = 256;
+constexpr int kMultiVpt = 8;
 
 struct KernelEntry {
     int op;        // Op
@@ -64,6 +71,7 @@ struct KernelEntry {
     RowtileLaunch rowtile;
     SplitLaunch split;
     OccupancyQuery occupancy;
+    MultipassLaunch multipass;
 };
 
 // The table of compiled kernels (defined in snr_kernels.hip).

@@ -477,6 +477,133 @@ split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-pass kernels for rows too wide to keep on chip (more chunks than
+// co-resident workgroups). Each pass is a plain grid; partial sums go
+// through device memory and are added in chunk order, so results stay
+// deterministic. These passes read a row more than once:
+//   plain: partial(x) -> combine -> y = x * inv * g                  (x twice)
+//   tail:  partial(a) -> combine -> h = r + a*inv_a*gp, partial(h) ->
+//          combine -> y = h * inv_h * gq                      (a and h twice)
+// ---------------------------------------------------------------------------
+constexpr int MB = 256;           // threads per workgroup
+constexpr int MVPT = 8;           // vectors per thread per chunk
+
+// Lane-strided chunk walk: vectors c*MB*MVPT + k*MB + tid, and in the last
+// chunk the remainder element tid.
+template <int ST, class F, class G>
+__device__ __forceinline__ void for_chunk(const RowArgs &p, int chunk,
+                                          int chunks, F vec_fn, G rem_fn) {
+    const int tid = threadIdx.x;
+    const int base = chunk * (MB * MVPT) + tid;
+#pragma unroll
+    for (int k = 0; k < MVPT; ++k) {
+        const int i = base + k * MB;
+        if (i < p.nv) vec_fn(i);
+    }
+    if (chunk == chunks - 1 && tid < p.rem) rem_fn(p.nv * Codec<ST>::W + tid);
+}
+
+// part[rl * chunks + c] = sum of squares of chunk c of row row0 + rl of `src`.
+template <int ST>
+__global__ void __launch_bounds__(MB)
+pass_sumsq(RowArgs p, const void *src, int64_t row0, int chunks, float *part) {
+    using C = Codec<ST>;
+    using T = typename C::T;
+    constexpr int W = C::W;
+    __shared__ float red[MB / 64];
+    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
+    const int64_t rl = blockIdx.x / (unsigned)chunks;
+    const T *x = static_cast<const T *>(src) + (row0 + rl) * (int64_t)p.n;
+    float s = 0.0f;
+    for_chunk<ST>(
+        p, chunk, chunks,
+        [&](int i) { float v[W]; C::load_nt(x, i, v); s += sumsq<W>(v); },
+        [&](int j) { const float v = C::load1_nt(x, j); s = fmaf(v, v, s); });
+    const float t = block_total(s, red);
+    if (threadIdx.x == 0) part[rl * chunks + chunk] = t;
+}
+
+// inv[rl] = 1/sqrt(sum_c part[rl * chunks + c] / n + eps), one workgroup per
+// row; lane l adds chunks l, l + 256, ... in order, then the lanes' sums are
+// added in a fixed order.
+__global__ void __launch_bounds__(MB)
+pass_combine(const float *part, int chunks, int n, float eps, float *inv) {
+    __shared__ float red[MB / 64];
+    const int64_t rl = blockIdx.x;
+    float s = 0.0f;
+    for (int c = threadIdx.x; c < chunks; c += MB) s += part[rl * chunks + c];
+    const float t = block_total(s, red);
+    if (threadIdx.x == 0) inv[rl] = inv_rms(t, n, eps);
+}
+
+// plain: y = x * inv * g.
+template <int ST>
+__global__ void __launch_bounds__(MB)
+pass_scale(RowArgs p, const void *src, const void *gain, void *dst,
+           int64_t row0, int chunks, const float *inv) {
+    using C = Codec<ST>;
+    using T = typename C::T;
+    constexpr int W = C::W;
+    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
+    const int64_t rl = blockIdx.x / (unsigned)chunks;
+    const int64_t off = (row0 + rl) * (int64_t)p.n;
+    const T *x = static_cast<const T *>(src) + off;
+    const T *g = static_cast<const T *>(gain);
+    T *y = static_cast<T *>(dst) + off;
+    const float r = inv[rl];
+    for_chunk<ST>(
+        p, chunk, chunks,
+        [&](int i) {
+            float v[W], gv[W], o[W];
+            C::load_nt(x, i, v);
+            C::load(g, i, gv);
+#pragma unroll
+            for (int e = 0; e < W; ++e) o[e] = v[e] * r * gv[e];
+            C::store_nt(y, i, o);
+        },
+        [&](int j) { C::store1_nt(y, j, C::load1_nt(x, j) * r * C::load1(g, j)); });
+}
+
+// tail: h = r + a * inv_a * gamma_post, stored, with its chunk's sum of
+// squares in part[rl * chunks + c].
+__global__ void __launch_bounds__(MB)
+pass_residual(RowArgs p, int64_t row0, int chunks, const float *inv,
+              float *part) {
+    using C = Codec<ST_F32>;
+    constexpr int W = C::W;
+    __shared__ float red[MB / 64];
+    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
+    const int64_t rl = blockIdx.x / (unsigned)chunks;
+    const int64_t off = (row0 + rl) * (int64_t)p.n;
+    const float *a = static_cast<const float *>(p.x0) + off;
+    const float *r = static_cast<const float *>(p.x1) + off;
+    const float *g = static_cast<const float *>(p.g0);
+    float *h = static_cast<float *>(p.out0) + off;
+    const float ia = inv[rl];
+    float s = 0.0f;
+    for_chunk<ST_F32>(
+        p, chunk, chunks,
+        [&](int i) {
+            float av[W], rv[W], gv[W], hv[W];
+            C::load_nt(a, i, av);
+            C::load_nt(r, i, rv);
+            C::load(g, i, gv);
+#pragma unroll
+            for (int e = 0; e < W; ++e) hv[e] = fmaf(av[e] * ia, gv[e], rv[e]);
+            C::store_nt(h, i, hv);
+            s += sumsq<W>(hv);
+        },
+        [&](int j) {
+            const float hv = fmaf(C::load1_nt(a, j) * ia, C::load1(g, j),
+                                  C::load1_nt(r, j));
+            C::store1_nt(h, j, hv);
+            s = fmaf(hv, hv, s);
+        });
+    const float t = block_total(s, red);
+    if (threadIdx.x == 0) part[rl * chunks + chunk] = t;
+}
+
 __global__ void zero_kernel(unsigned int *p, int64_t words) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -525,17 +652,48 @@ hipError_t occupancy_split(int *blocks_per_cu) {
         blocks_per_cu, split_kernel<OP, ST, VPT>, SB, 0);
 }
 
+// Multi-pass launch over rows [row0, row0 + nrows): scratch holds
+// nrows * chunks partial sums followed by nrows inverse norms.
+template <int OP, int ST>
+hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
+                            int64_t nrows, int chunks, hipStream_t stream) {
+    float *part = scratch;
+    float *inv = scratch + nrows * (int64_t)chunks;
+    const dim3 grid((unsigned int)(nrows * chunks)), rows_grid((unsigned int)nrows);
+    hipLaunchKernelGGL(pass_sumsq<ST>, grid, dim3(MB), 0, stream, p, p.x0,
+                       row0, chunks, part);
+    hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
+                       (const float *)part, chunks, p.n, p.eps0, inv);
+    if constexpr (OP == OP_PLAIN) {
+        hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p, p.x0,
+                           p.g0, p.out0, row0, chunks, (const float *)inv);
+    } else {
+        hipLaunchKernelGGL(pass_residual, grid, dim3(MB), 0, stream, p, row0,
+                           chunks, (const float *)inv, part);
+        hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
+                           (const float *)part, chunks, p.n, p.eps1, inv);
+        hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p,
+                           (const void *)p.out0, p.g1, p.out1, row0, chunks,
+                           (const float *)inv);
+    }
+    return hipGetLastError();
+}
+
 #define SNR_RT(OP, ST, G, VPT)                                              \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
                 rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
-                nullptr, &occupancy_rowtile<OP, ST, G, VPT>}
+                nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr}
 #define SNR_RT_LATE(G, VPT)                                                 \
     KernelEntry{OP_TAIL, ST_F32, 4, KIND_ROWTILE, G, VPT, rowtile_block<G>(), \
                 &launch_rowtile<OP_TAIL, ST_F32, G, VPT, true>, nullptr,    \
-                &occupancy_rowtile<OP_TAIL, ST_F32, G, VPT, true>}
+                &occupancy_rowtile<OP_TAIL, ST_F32, G, VPT, true>, nullptr}
 #define SNR_SPLIT(OP, ST, VPT)                                              \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, VPT, SB, nullptr,      \
-                &launch_split<OP, ST, VPT>, &occupancy_split<OP, ST, VPT>}
+                &launch_split<OP, ST, VPT>, &occupancy_split<OP, ST, VPT>,   \
+                nullptr}
+#define SNR_MULTI(OP, ST)                                                   \
+    KernelEntry{OP, ST, Codec<ST>::W, KIND_MULTIPASS, MB, MVPT, MB, nullptr, \
+                nullptr, nullptr, &launch_multipass<OP, ST>}
 
 // The shapes compiled for one (operation, storage). Sub-wavefront groups
 // hold 4 vectors per lane; whole wavefronts and workgroups hold up to 16.
@@ -548,7 +706,7 @@ hipError_t occupancy_split(int *blocks_per_cu) {
     SNR_RT(OP, ST, 256, 8), SNR_RT(OP, ST, 256, 16), SNR_RT(OP, ST, 512, 4), \
     SNR_RT(OP, ST, 512, 8), SNR_RT(OP, ST, 512, 16),                        \
     SNR_RT(OP, ST, 1024, 2), SNR_RT(OP, ST, 1024, 4),                       \
-    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST, 8)
+    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST, 8), SNR_MULTI(OP, ST)
 
 // 1024 lanes x 16 vectors only where the row fits in the 128 registers a
 // lane of a 1024-lane workgroup may use: not for 8-wide bf16, and for the

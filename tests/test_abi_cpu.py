@@ -60,6 +60,7 @@ def test_error_codes_match_header():
         assert header_enum(name) == getattr(_lib, name), name
     assert header_enum("SNR_SHAPE_ROWTILE") == _lib.SHAPE_ROWTILE
     assert header_enum("SNR_SHAPE_SPLIT") == _lib.SHAPE_SPLIT
+    assert header_enum("SNR_SHAPE_MULTIPASS") == _lib.SHAPE_MULTIPASS
 
 
 def test_strerror_covers_every_code(L):

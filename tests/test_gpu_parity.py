@@ -196,6 +196,51 @@ def test_split_full_size(oracle, name):
     assert snr.split_timeouts() == 0
 
 
+@pytest.mark.parametrize("op_st", [("plain", "f32"), ("plain", "bf16"),
+                                   ("tail", "f32")])
+@pytest.mark.parametrize("n", [1, 3, 100, 6657, 2048 * 8 * 3 + 5])
+def test_forced_multipass(oracle, op_st, n):
+    op, st = op_st
+    w = VEC[st]
+    rows = 7
+    chunks = max(1, -(-(n // w) // 2048))
+    say(f"forced multipass {op} {st} rows={rows} n={n}")
+    with snr.forced_shape("multipass"):
+        if op == "plain":
+            inp = gen.random_plain(rows, n, 9900 + n, dtype=st)
+            got, _ = run_plain(inp)
+            shape = snr.last_shape()
+            check_plain(oracle, inp, got, f"multipass-{op}-{st}-{n}")
+        else:
+            inp = gen.random_tail(rows, n, 9901 + n)
+            h, y = run_tail(inp)
+            shape = snr.last_shape()
+            check_tail(oracle, inp, h, y, f"multipass-tail-{n}")
+    assert shape == f"multipass:256:8:{w}:{chunks}", shape
+
+
+@pytest.mark.parametrize("op_st_n", [("plain", "f32", 8192 * 1024 + 5),
+                                     ("tail", "f32", 8192 * 1024 + 5),
+                                     ("plain", "bf16", 8 * 2048 * 1025 + 3)])
+def test_rows_wider_than_the_split_capacity(oracle, op_st_n):
+    """Rows too wide for co-resident chunks fall back to the multi-pass
+    kernels automatically."""
+    op, st, n = op_st_n
+    rows = 2
+    say(f"very wide {op} {st} rows={rows} n={n}")
+    if op == "plain":
+        inp = gen.random_plain(rows, n, 9950, dtype=st)
+        got, _ = run_plain(inp)
+        shape = snr.last_shape()
+        check_plain(oracle, inp, got, f"wide-{op}-{st}")
+    else:
+        inp = gen.random_tail(rows, n, 9951)
+        h, y = run_tail(inp)
+        shape = snr.last_shape()
+        check_tail(oracle, inp, h, y, "wide-tail")
+    assert shape.startswith("multipass:256:8:"), shape
+
+
 def test_forced_shape_that_cannot_hold_the_row_is_refused():
     x = torch.zeros(4, 4096, device=DEV)
     g = torch.ones(4096, device=DEV)
