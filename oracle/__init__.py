@@ -19,6 +19,10 @@ Definitions followed (cited by page title and section):
 * ``sandwich_tail``: same page, section 12.2 (sandwich order) and section
   12.4.3 (the dual-epsilon fused tail): h = r + rmsnorm(a, gamma_post,
   eps_post); y = rmsnorm(h, gamma_pre, eps_pre), with h kept in f64.
+* ``norm_then_add``: Hesper "RMSNorm Layer" page, rmsNormThenAddKernel and
+  rmsNormThenAddThenBroadcastScaleKernel: (rmsnorm(a) + r) * scale.
+* ``add_then_norm``: same page, residualAddRmsNormKernel: s = a + b and
+  rmsnorm(s), both returned, s kept in f64.
 """
 from __future__ import annotations
 
@@ -78,8 +82,14 @@ class Oracle:
         lib.snr_oracle_sandwich_tail.argtypes = [vp, vp, vp, ctypes.c_float,
                                                  vp, ctypes.c_float, _i64,
                                                  _i64, vp, vp, vp, vp, vp, vp]
+        lib.snr_oracle_norm_then_add.argtypes = [vp, vp, vp, ctypes.c_float,
+                                                 ctypes.c_double, _i64, _i64,
+                                                 vp, vp, vp]
+        lib.snr_oracle_add_then_norm.argtypes = [vp, vp, vp, ctypes.c_float,
+                                                 _i64, _i64, vp, vp, vp, vp]
         for f in (lib.snr_oracle_rmsnorm_f32, lib.snr_oracle_rmsnorm_bf16,
-                  lib.snr_oracle_sandwich_tail):
+                  lib.snr_oracle_sandwich_tail, lib.snr_oracle_norm_then_add,
+                  lib.snr_oracle_add_then_norm):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -136,6 +146,48 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected arguments (code {rc})")
         return TailResult(h, y, p, d_a, d_h)
+
+
+    # -- the tail's two halves ------------------------------------------
+    def norm_then_add(self, a: np.ndarray, r: np.ndarray, gamma: np.ndarray,
+                      eps: float, scale: float | None = None):
+        """(a / sqrt(mean(a^2) + eps) * gamma + r) * scale, f64; float32
+        inputs. Returns (out, d) with d the per-row denominator."""
+        a, r, gamma = (np.ascontiguousarray(v, dtype=np.float32)
+                       for v in (a, r, gamma))
+        if a.ndim != 2 or r.shape != a.shape or gamma.shape != (a.shape[1],):
+            raise ValueError("a, r must be [rows, n] and gamma [n]")
+        rows, n = a.shape
+        out = np.empty((rows, n), np.float64)
+        d = np.empty(rows, np.float64)
+        work = np.empty(2 * max(n, 1), np.float64)
+        rc = self._lib.snr_oracle_norm_then_add(
+            _ptr(a), _ptr(r), _ptr(gamma), float(eps),
+            1.0 if scale is None else float(scale), rows, n, _ptr(out),
+            _ptr(d), _ptr(work))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (code {rc})")
+        return out, d
+
+    def add_then_norm(self, a: np.ndarray, b: np.ndarray, gamma: np.ndarray,
+                      eps: float):
+        """s = a + b; y = s / sqrt(mean(s^2) + eps) * gamma, f64; float32
+        inputs. Returns (s, y, d)."""
+        a, b, gamma = (np.ascontiguousarray(v, dtype=np.float32)
+                       for v in (a, b, gamma))
+        if a.ndim != 2 or b.shape != a.shape or gamma.shape != (a.shape[1],):
+            raise ValueError("a, b must be [rows, n] and gamma [n]")
+        rows, n = a.shape
+        s = np.empty((rows, n), np.float64)
+        y = np.empty((rows, n), np.float64)
+        d = np.empty(rows, np.float64)
+        work = np.empty(2 * max(n, 1), np.float64)
+        rc = self._lib.snr_oracle_add_then_norm(
+            _ptr(a), _ptr(b), _ptr(gamma), float(eps), rows, n, _ptr(s),
+            _ptr(y), _ptr(d), _ptr(work))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (code {rc})")
+        return s, y, d
 
 
 _DEFAULT: Oracle | None = None

@@ -165,3 +165,66 @@ int snr_oracle_sandwich_tail(const float *a, const float *r,
     }
     return ORACLE_OK;
 }
+
+/*
+ * The first half of the tail on its own: post-norm of a sub-block's output
+ * added to the residual, optionally times a broadcast scalar. Hesper's
+ * "RMSNorm Layer" page (rmsNormThenAddKernel, the Gemma-4 post-norm shape,
+ * and rmsNormThenAddThenBroadcastScaleKernel): normalise the block output
+ * first, then add the residual, then multiply by out_scale:
+ *   d   = sqrt(mean(a^2) + eps)
+ *   out = (a / d * gamma + r) * scale        (scale = 1 when absent)
+ * Inputs f32 (callers decode other storage exactly); out in double.
+ * work: 2*n doubles.
+ */
+int snr_oracle_norm_then_add(const float *a, const float *r,
+                             const float *gamma, float eps, double scale,
+                             int64_t rows, int64_t n, double *out,
+                             double *d_out, double *work)
+{
+    if (n < 1 || rows < 0 || !a || !r || !gamma || !out || !work)
+        return ORACLE_EBADARG;
+    double *ar = work, *gr = work + n;
+    for (int64_t j = 0; j < n; ++j)
+        gr[j] = (double)gamma[j];
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            ar[j] = (double)a[i * n + j];
+        double *oi = out + i * n;
+        const double d = rms_row(ar, gr, (double)eps, n, oi);
+        for (int64_t j = 0; j < n; ++j)
+            oi[j] = (oi[j] + (double)r[i * n + j]) * scale;
+        if (d_out)
+            d_out[i] = d;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The second half on its own: residual add, then RMSNorm of the sum, writing
+ * both. Hesper's "RMSNorm Layer" page, residualAddRmsNormKernel: each row
+ * forms residualOut = a + b, reduces it, and writes residualOut and
+ * output = RMSNorm(residualOut) * scale.
+ *   s = a + b;  y = s / sqrt(mean(s^2) + eps) * gamma
+ * s is kept in double. work: 2*n doubles.
+ */
+int snr_oracle_add_then_norm(const float *a, const float *b,
+                             const float *gamma, float eps, int64_t rows,
+                             int64_t n, double *sum, double *y,
+                             double *d_out, double *work)
+{
+    if (n < 1 || rows < 0 || !a || !b || !gamma || !sum || !y || !work)
+        return ORACLE_EBADARG;
+    double *gr = work;
+    for (int64_t j = 0; j < n; ++j)
+        gr[j] = (double)gamma[j];
+    for (int64_t i = 0; i < rows; ++i) {
+        double *si = sum + i * n;
+        for (int64_t j = 0; j < n; ++j)
+            si[j] = (double)a[i * n + j] + (double)b[i * n + j];
+        const double d = rms_row(si, gr, (double)eps, n, y + i * n);
+        if (d_out)
+            d_out[i] = d;
+    }
+    return ORACLE_OK;
+}

@@ -378,6 +378,128 @@ def pin_decimal_tail(O):
         assert abs(t.d_h[0] - float(d_h)) <= 1e-14 * float(d_h)
 
 
+# ---------------------------------------------------------------------------
+# The tail's two halves (Hesper "RMSNorm Layer": rmsNormThenAdd[...]Kernel,
+# residualAddRmsNormKernel)
+# ---------------------------------------------------------------------------
+
+def pin_norm_then_add_closed_forms(O):
+    """a = 0 gives out = r * scale exactly; r = 0 gives rmsnorm(a) * scale;
+    the hand example a = [3, 4], r = [1, -1], scale 2."""
+    rng = rng_for(31)
+    for n in (1, 2, 7, 130):
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        r = rng.standard_normal((3, n)).astype(F32)
+        a = (rng.standard_normal((3, n)) * 10).astype(F32)
+        for scale in (None, 2.0, -0.5):
+            sc = 1.0 if scale is None else scale
+            out, _ = O.norm_then_add(np.zeros_like(a), r, g, 1e-8, scale)
+            assert np.array_equal(out, r.astype(np.float64) * sc)
+            out, _ = O.norm_then_add(a, np.zeros_like(r), g, 1e-8, scale)
+            assert np.array_equal(out, O.rmsnorm(a, g, 1e-8) * sc)
+    ep = _f(1e-8)
+    d = math.sqrt(12.5 + ep)
+    want = [(3 / d + 1) * 2, (4 / d - 1) * 2]
+    out, dd = O.norm_then_add(np.array([[3, 4]], F32),
+                              np.array([[1, -1]], F32), np.ones(2, F32), 1e-8,
+                              2.0)
+    assert np.all(np.abs(out[0] - want) <= 4e-15 * (np.abs(want) + 2))
+    assert abs(dd[0] - d) <= 1e-15 * d
+    assert abs(out[0, 0] - 3.697056274168) < 1e-11
+
+
+def pin_add_then_norm_closed_forms(O):
+    """b = 0 gives s = a and y = rmsnorm(a) exactly; b = -a gives zeros; the
+    hand example a = [3, 4], b = [1, -1] (s = [4, 3])."""
+    rng = rng_for(32)
+    for n in (1, 3, 64):
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        a = (rng.standard_normal((2, n)) * 3).astype(F32)
+        s, y, _ = O.add_then_norm(a, np.zeros_like(a), g, 1e-5)
+        assert np.array_equal(s, a.astype(np.float64))
+        assert np.array_equal(y, O.rmsnorm(a, g, 1e-5))
+        s, y, _ = O.add_then_norm(a, -a, g, 1e-5)
+        assert np.all(s == 0) and np.all(y == 0)
+    e = _f(1e-5)
+    d = math.sqrt(12.5 + e)
+    s, y, dd = O.add_then_norm(np.array([[3, 4]], F32),
+                               np.array([[1, -1]], F32), np.ones(2, F32), 1e-5)
+    assert np.array_equal(s[0], [4.0, 3.0])
+    assert np.max(_rel(y[0], [4 / d, 3 / d])) < 2e-15
+    assert abs(y[0, 0] - 1.131370397350) < 1e-11
+
+
+def pin_halves_compose_to_the_tail(O):
+    """The tail's h is norm_then_add(a, r) with the post-norm gain and
+    epsilon; add_then_norm on an exactly representable sum equals rmsnorm of
+    that sum."""
+    rng = rng_for(33)
+    for n in (2, 9, 300):
+        a = rng.standard_normal((4, n)).astype(F32)
+        r = rng.standard_normal((4, n)).astype(F32)
+        gp = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        gq = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        t = O.sandwich_tail(a, r, gp, 1e-8, gq, 1e-5)
+        out, d = O.norm_then_add(a, r, gp, 1e-8)
+        assert np.array_equal(out, t.h) and np.array_equal(d, t.d_a)
+        ai = rng.integers(-50, 50, (3, n)).astype(F32)
+        bi = rng.integers(-50, 50, (3, n)).astype(F32)
+        s, y, _ = O.add_then_norm(ai, bi, gq, 1e-5)
+        assert np.array_equal(y, O.rmsnorm((ai + bi).astype(F32), gq, 1e-5))
+
+
+def pin_halves_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = rng_for(34)
+    for n in (5, 128, 6656):
+        a = (rng.standard_normal((3, n)) * 10.0 ** rng.uniform(-3, 2)).astype(F32)
+        b = rng.standard_normal((3, n)).astype(F32)
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        tg = torch.from_numpy(g).double()
+        ta, tb = torch.from_numpy(a).double(), torch.from_numpy(b).double()
+        want = (F.rms_norm(ta, (n,), tg, eps=_f(1e-8)) + tb) * 0.75
+        out, _ = O.norm_then_add(a, b, g, 1e-8, 0.75)
+        assert np.max(np.abs(out - want.numpy()) /
+                      (np.abs(want.numpy()) + 1.0)) < 1e-13
+        s, y, _ = O.add_then_norm(a, b, g, 1e-5)
+        want = F.rms_norm(ta + tb, (n,), tg, eps=_f(1e-5)).numpy()
+        assert np.max(_rel(y, want)) < 1e-12
+
+
+def pin_decimal_halves(O):
+    getcontext().prec = 50
+    rng = rng_for(35)
+    for i in range(40):
+        n = int(rng.integers(1, 17))
+        a = (rng.standard_normal(n) * 10.0 ** rng.choice([-4.0, -2.0, 0.0, 1.0])
+             ).astype(F32)
+        r = (rng.standard_normal(n) * 10.0 ** rng.choice([-3.0, -1.0, 0.5])
+             ).astype(F32)
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        scale = float(rng.choice([1.0, 0.5, 3.0]))
+        eps = float(rng.choice([1e-8, 1e-5]))
+        ad = [Decimal(float(v)) for v in a]
+        rd = [Decimal(float(v)) for v in r]
+        gd = [Decimal(float(v)) for v in g]
+        p, _ = _dec_rms(ad, gd, Decimal(_f(eps)))
+        want = np.array([float((pv + rv) * Decimal(scale))
+                         for pv, rv in zip(p, rd)])
+        out, _ = O.norm_then_add(a[None, :], r[None, :], g, eps, scale)
+        sc = (np.abs([float(v) for v in p]) + np.abs(r)) * abs(scale)
+        assert np.all(np.abs(out[0] - want) <= 1e-14 * sc + 1e-300), i
+        sd = [x + y for x, y in zip(ad, rd)]
+        yd, dd = _dec_rms(sd, gd, Decimal(_f(eps)))
+        s, y, d = O.add_then_norm(a[None, :], r[None, :], g, eps)
+        sc = np.abs(a.astype(np.float64)) + np.abs(r)
+        assert np.all(np.abs(s[0] - np.array([float(v) for v in sd]))
+                      <= 1e-15 * sc), i
+        ysc = np.abs(g.astype(np.float64)) * sc / float(dd)
+        assert np.all(np.abs(y[0] - np.array([float(v) for v in yd]))
+                      <= 1e-14 * ysc + 1e-300), i
+        assert abs(d[0] - float(dd)) <= 1e-14 * float(dd)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_constant_rows,
@@ -394,4 +516,9 @@ ALL_PINS = [
     pin_decimal_plain,
     pin_decimal_bf16,
     pin_decimal_tail,
+    pin_norm_then_add_closed_forms,
+    pin_add_then_norm_closed_forms,
+    pin_halves_compose_to_the_tail,
+    pin_halves_torch,
+    pin_decimal_halves,
 ]

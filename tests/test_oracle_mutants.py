@@ -43,6 +43,14 @@ MUTANTS = {
                           "uint32_t u = (uint32_t)b << 15;"),
     "bf16_gamma_as_one": ("gr[j] = (double)bf16_bits_to_f32(gamma[j]);",
                           "gr[j] = 1.0;"),
+    "scale_only_on_norm": ("oi[j] = (oi[j] + (double)r[i * n + j]) * scale;",
+                           "oi[j] = oi[j] * scale + (double)r[i * n + j];"),
+    "norm_add_subtracts": ("oi[j] = (oi[j] + (double)r[i * n + j]) * scale;",
+                           "oi[j] = (oi[j] - (double)r[i * n + j]) * scale;"),
+    "add_norm_subtracts": ("si[j] = (double)a[i * n + j] + (double)b[i * n + j];",
+                           "si[j] = (double)a[i * n + j] - (double)b[i * n + j];"),
+    "add_norm_drops_b": ("si[j] = (double)a[i * n + j] + (double)b[i * n + j];",
+                         "si[j] = (double)a[i * n + j];"),
 }
 
 
