@@ -38,10 +38,14 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# row streams (reads + writes) and gains of each operation
+STREAMS = {"plain": (2, 1), "tail": (4, 2), "norm_add": (3, 1),
+           "add_norm": (4, 1)}
+
+
 def algorithmic_bytes(cfg) -> int:
-    es = 2 if cfg.dtype == "bf16" else 4
-    streams = 4 if cfg.kind == "tail" else 2
-    gains = 2 if cfg.kind == "tail" else 1
+    es = 4 if cfg.dtype == "f32" else 2
+    streams, gains = STREAMS[cfg.kind]
     return streams * cfg.rows * cfg.n * es + gains * cfg.n * es
 
 
@@ -75,36 +79,60 @@ def measured_traffic(cfg, shape):
     return float(kv["traffic_bytes_per_launch"])
 
 
-def make_device_sets(cfg, inp, sets, torch):
+def to_device(arr, dtype, torch):
+    """A storage array (float32, or uint16 bits of bf16/f16) on cuda:0."""
+    import numpy as np
     dev = torch.device("cuda:0")
+    if dtype == "f32":
+        return torch.from_numpy(arr).to(dev)
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev)
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def make_device_sets(cfg, inp, sets, torch):
+    """`sets` copies of the row inputs and their own outputs; gains shared."""
+    st = cfg.dtype
+    rows_keys = {"plain": ("x",), "tail": ("a", "r"),
+                 "norm_add": ("a", "b"), "add_norm": ("a", "b")}[cfg.kind]
+    gain_keys = ("gamma_post", "gamma_pre") if cfg.kind == "tail" else \
+        ("gamma",)
+    nout = {"plain": 1, "tail": 2, "norm_add": 1, "add_norm": 2}[cfg.kind]
+    base = {k: to_device(inp[k], st, torch) for k in rows_keys + gain_keys}
     out = []
-    if cfg.kind == "tail":
-        base = {k: torch.from_numpy(inp[k]).to(dev)
-                for k in ("a", "r", "gamma_post", "gamma_pre")}
-        for _ in range(sets):
-            out.append({"a": base["a"].clone(), "r": base["r"].clone(),
-                        "gp": base["gamma_post"], "gq": base["gamma_pre"],
-                        "h": torch.empty_like(base["a"]),
-                        "y": torch.empty_like(base["a"])})
-    else:
-        import numpy as np
-        if cfg.dtype == "bf16":
-            x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(
-                torch.bfloat16)
-            g = torch.from_numpy(inp["gamma"].view(np.int16)).to(dev).view(
-                torch.bfloat16)
-        else:
-            x = torch.from_numpy(inp["x"]).to(dev)
-            g = torch.from_numpy(inp["gamma"]).to(dev)
-        for _ in range(sets):
-            out.append({"x": x.clone(), "g": g, "y": torch.empty_like(x)})
+    for _ in range(sets):
+        d = {k: base[k].clone() for k in rows_keys}
+        d.update({k: base[k] for k in gain_keys})
+        d["out"] = [torch.empty_like(base[rows_keys[0]]) for _ in range(nout)]
+        out.append(d)
     return out
+
+
+def make_step(cfg, inp, sets, snr):
+    kind = cfg.kind
+
+    def step(i):
+        s = sets[i % len(sets)]
+        if kind == "tail":
+            snr.sandwich_tail(s["a"], s["r"], s["gamma_post"],
+                              inp["eps_post"], s["gamma_pre"], inp["eps_pre"],
+                              h_out=s["out"][0], y_out=s["out"][1])
+        elif kind == "plain":
+            snr.rmsnorm_fwd(s["x"], s["gamma"], inp["eps"], out=s["out"][0])
+        elif kind == "norm_add":
+            snr.norm_then_add(s["a"], s["b"], s["gamma"], inp["eps"],
+                              out=s["out"][0])
+        else:
+            snr.add_then_norm(s["a"], s["b"], s["gamma"], inp["eps"],
+                              sum_out=s["out"][0], y_out=s["out"][1])
+    return step
 
 
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
     """The f64 oracle as it stands, rows split across host threads (ctypes
     releases the GIL), repeated over the full workload for about `seconds`."""
     from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
 
     import oracle
     O = oracle.load()
@@ -114,14 +142,24 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
               for i in range(cores)]
     bounds = [b for b in bounds if b[1] > b[0]]
 
+    from sandwich_norm_residual_amd.inputs import from_storage
+    st = cfg.dtype
+    f = {k: from_storage(v, st) for k, v in inp.items()
+         if isinstance(v, np.ndarray)}
+
     def one(b):
         lo, hi = b
         if cfg.kind == "tail":
-            O.sandwich_tail(inp["a"][lo:hi], inp["r"][lo:hi],
-                            inp["gamma_post"], inp["eps_post"],
-                            inp["gamma_pre"], inp["eps_pre"])
+            O.sandwich_tail(f["a"][lo:hi], f["r"][lo:hi], f["gamma_post"],
+                            inp["eps_post"], f["gamma_pre"], inp["eps_pre"])
+        elif cfg.kind == "plain":
+            O.rmsnorm(f["x"][lo:hi], f["gamma"], inp["eps"])
+        elif cfg.kind == "norm_add":
+            O.norm_then_add(f["a"][lo:hi], f["b"][lo:hi], f["gamma"],
+                            inp["eps"])
         else:
-            O.rmsnorm(inp["x"][lo:hi], inp["gamma"], inp["eps"])
+            O.add_then_norm(f["a"][lo:hi], f["b"][lo:hi], f["gamma"],
+                            inp["eps"])
 
     passes = 0
     t0 = time.perf_counter()
@@ -191,14 +229,7 @@ def main() -> int:
     stream = torch.cuda.Stream()   # default priority
     nbytes = algorithmic_bytes(cfg)
 
-    def step(i):
-        s = sets[i % len(sets)]
-        if cfg.kind == "tail":
-            snr.sandwich_tail(s["a"], s["r"], s["gp"], inp["eps_post"],
-                              s["gq"], inp["eps_pre"], h_out=s["h"],
-                              y_out=s["y"])
-        else:
-            snr.rmsnorm_fwd(s["x"], s["g"], inp["eps"], out=s["y"])
+    step = make_step(cfg, inp, sets, snr)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):

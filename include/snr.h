@@ -43,9 +43,13 @@ typedef struct ihipStream_t *hipStream_t;
 
 typedef enum {
     SNR_F32 = 0,  /* IEEE binary32 storage */
-    SNR_BF16 = 1  /* bfloat16 storage; arithmetic in f32, output rounded to
-                     nearest-even */
+    SNR_BF16 = 1, /* bfloat16 storage */
+    SNR_F16 = 2   /* IEEE binary16 storage */
 } snr_dtype;
+/* Every operation reads its storage type exactly into f32, accumulates and
+ * computes in f32, and rounds its outputs to the storage type to nearest
+ * even. An intermediate that a later norm of the same call reads (the
+ * tail's h, add_then_norm's sum) is normalised as it is stored. */
 
 enum {
     SNR_OK = 0,
@@ -78,17 +82,16 @@ enum {
  *   eps    epsilon added to the mean of squares; finite and > 0
  *   rows   number of rows (>= 0)
  *   n      row width (>= 1)
- *   dtype  SNR_F32 or SNR_BF16 (storage of x, gamma and y). Accumulation and
- *          arithmetic are f32 in both cases; bf16 output is rounded to
- *          nearest-even.
+ *   dtype  SNR_F32, SNR_BF16 or SNR_F16 (storage of x, gamma and y)
  *   y      [rows, n] output, dtype `dtype`. y == x (exactly the same
  *          pointer) is allowed and computes in place; any other overlap of y
  *          with x or gamma is SNR_ERR_ALIAS.
  *   stream HIP stream to enqueue on (NULL = default stream)
  *
- * Pointers need only element alignment (4 B for f32, 2 B for bf16). Rows
- * are moved with 128-bit accesses whatever their alignment; the n % 4 (f32)
- * or n % 8 (bf16) elements after a row's last whole vector one at a time.
+ * Pointers need only element alignment (4 B for f32, 2 B for 16-bit types).
+ * Rows are moved with 128-bit accesses whatever their alignment; the n % 4
+ * (f32) or n % 8 (16-bit) elements after a row's last whole vector one at a
+ * time.
  */
 SNR_API int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
                 int64_t n, int dtype, void *y, hipStream_t stream);
@@ -126,6 +129,61 @@ SNR_API int sandwich_tail(const float *a, const float *r, const float *gamma_pos
                   float eps_post, const float *gamma_pre, float eps_pre,
                   float *h_out, float *y_out, int64_t rows, int64_t n,
                   hipStream_t stream);
+
+/*
+ * sandwich_tail_typed - the same tail for any snr_dtype storage: a, r, both
+ * gains, h_out and y_out all of type `dtype`. With bf16 or f16 storage, h is
+ * rounded to the storage type before its norm (y = norm of h as stored).
+ * Same aliasing rules as sandwich_tail.
+ *
+ * sandwich_tail_inplace - the tail with the residual stream updated in place
+ * (the Muser kernel's form, where `hidden` is read and written, and Hesper's
+ * forwardNormThenAddBatchInPlace): residual <- residual + post-norm(a), and
+ * y_out <- pre-norm of the updated residual. y_out may not overlap any other
+ * buffer; residual may not overlap a or the gains.
+ */
+SNR_API int sandwich_tail_typed(const void *a, const void *r,
+                                const void *gamma_post, float eps_post,
+                                const void *gamma_pre, float eps_pre,
+                                void *h_out, void *y_out, int64_t rows,
+                                int64_t n, int dtype, hipStream_t stream);
+SNR_API int sandwich_tail_inplace(const void *a, void *residual,
+                                  const void *gamma_post, float eps_post,
+                                  const void *gamma_pre, float eps_pre,
+                                  void *y_out, int64_t rows, int64_t n,
+                                  int dtype, hipStream_t stream);
+
+/*
+ * norm_then_add - the first half of the tail on its own: post-norm of a
+ * sub-block's output, added to the residual, optionally times a broadcast
+ * scalar. Defined on Hesper's "RMSNorm Layer" page (rmsNormThenAddKernel,
+ * the Gemma-4 post-norm shape, its batched row-major form
+ * rmsNormAddBatchRowsKernel, and rmsNormThenAddThenBroadcastScaleKernel):
+ *     out = (a / sqrt(mean(a^2) + eps) * gamma + r) * out_scale[0]
+ *   a, r      [rows, n] of `dtype`;  gamma [n] of `dtype`
+ *   out_scale device pointer to one f32 value, or NULL for 1
+ *   out       [rows, n] of `dtype`; out == r (exactly) updates the residual
+ *             in place; any other overlap with a, r, gamma or out_scale is
+ *             SNR_ERR_ALIAS.
+ */
+SNR_API int norm_then_add(const void *a, const void *r, const void *gamma,
+                          float eps, const float *out_scale, void *out,
+                          int64_t rows, int64_t n, int dtype,
+                          hipStream_t stream);
+
+/*
+ * add_then_norm - the second half on its own: residual add, then RMSNorm of
+ * the sum, writing both. Hesper's "RMSNorm Layer" page,
+ * residualAddRmsNormKernel:
+ *     sum = a + b;  y = sum / sqrt(mean(sum^2) + eps) * gamma
+ *   a, b      [rows, n] of `dtype`;  gamma [n] of `dtype`
+ *   sum_out   [rows, n]; may coincide exactly with a or with b
+ *   y_out     [rows, n]; may overlap no other buffer
+ * With bf16 or f16 storage, y is the norm of the sum as stored.
+ */
+SNR_API int add_then_norm(const void *a, const void *b, const void *gamma,
+                          float eps, void *sum_out, void *y_out, int64_t rows,
+                          int64_t n, int dtype, hipStream_t stream);
 
 /* Human-readable text for an SNR_* code (static storage, never NULL). */
 SNR_API const char *snr_strerror(int code);

@@ -5,11 +5,17 @@ The compute is done by hand-written HIP kernels in ``libsnr.so`` behind a C
 ABI (``include/snr.h``); this module marshals torch tensors (device memory and
 the current stream) into those calls. Nothing here computes.
 
-    y    = rmsnorm_fwd(x, gamma, eps)                       # f32 or bf16
+    y    = rmsnorm_fwd(x, gamma, eps)              # f32, bf16 or f16
     h, y = sandwich_tail(a, r, gamma_post, eps_post, gamma_pre, eps_pre)
+    y    = sandwich_tail_inplace(a, residual, gamma_post, eps_post,
+                                 gamma_pre, eps_pre)   # residual updated
+    out  = norm_then_add(a, r, gamma, eps, out_scale=None)
+    s, y = add_then_norm(a, b, gamma, eps)
 
-Definitions ("RMSNorm and the dual-epsilon sandwich", Muser book chapter 12):
-section 12.1 for RMSNorm, sections 12.2 and 12.4.3 for the tail.
+Definitions: "RMSNorm and the dual-epsilon sandwich" (Muser book chapter
+12), section 12.1 for RMSNorm and sections 12.2 and 12.4.3 for the tail;
+Hesper's "RMSNorm Layer" page for norm_then_add (rmsNormThenAdd kernels)
+and add_then_norm (residualAddRmsNormKernel).
 """
 from __future__ import annotations
 
@@ -18,7 +24,8 @@ import contextlib
 from . import _lib
 from ._lib import SnrError
 
-__all__ = ["rmsnorm_fwd", "sandwich_tail", "forced_shape", "last_shape",
+__all__ = ["rmsnorm_fwd", "sandwich_tail", "sandwich_tail_inplace",
+           "norm_then_add", "add_then_norm", "forced_shape", "last_shape",
            "split_timeouts", "SnrError"]
 
 
@@ -33,7 +40,10 @@ def _dtype_code(t) -> int:
         return _lib.SNR_F32
     if t.dtype == torch.bfloat16:
         return _lib.SNR_BF16
-    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return _lib.SNR_F16
+    raise ValueError(f"unsupported dtype {t.dtype} "
+                     "(float32, bfloat16 or float16)")
 
 
 def _check_tensor(name, t, device, dtype, shape=None):
@@ -82,36 +92,115 @@ def rmsnorm_fwd(x, gamma, eps: float, out=None):
     return out
 
 
+def _stream(dev):
+    torch = _torch()
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _rows_inputs(names_tensors, gains, like):
+    """Check [..., n] inputs of one dtype/device and [n] gains."""
+    dev, dt = like.device, like.dtype
+    _dtype_code(like)
+    rows, n = _rows_n(like)
+    for name, t in names_tensors:
+        _check_tensor(name, t, dev, dt, like.shape)
+    for name, g in gains:
+        _check_tensor(name, g, dev, dt, (n,))
+    return rows, n
+
+
 def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
                   eps_pre: float, h_out=None, y_out=None):
-    """The fused dual-epsilon tail over the last dimension (float32):
+    """The fused dual-epsilon tail over the last dimension:
 
         h = r + gamma_post * a / sqrt(mean(a^2) + eps_post)
         y = gamma_pre * h / sqrt(mean(h^2) + eps_pre)
 
-    Returns (h, y). ``h_out is r`` updates the residual stream in place.
+    Tensors share one dtype (float32, bfloat16 or float16). Returns (h, y).
+    ``h_out is r`` updates the residual stream in place.
     """
     torch = _torch()
-    dev = a.device
-    f32 = torch.float32
-    _check_tensor("a", a, dev, f32)
-    rows, n = _rows_n(a)
-    _check_tensor("r", r, dev, f32, a.shape)
-    _check_tensor("gamma_post", gamma_post, dev, f32, (n,))
-    _check_tensor("gamma_pre", gamma_pre, dev, f32, (n,))
+    rows, n = _rows_inputs([("a", a), ("r", r)],
+                           [("gamma_post", gamma_post),
+                            ("gamma_pre", gamma_pre)], a)
     h_out = torch.empty_like(a) if h_out is None else h_out
     y_out = torch.empty_like(a) if y_out is None else y_out
-    _check_tensor("h_out", h_out, dev, f32, a.shape)
-    _check_tensor("y_out", y_out, dev, f32, a.shape)
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = _lib.sandwich_tail(a.data_ptr(), r.data_ptr(),
-                                gamma_post.data_ptr(), float(eps_post),
-                                gamma_pre.data_ptr(), float(eps_pre),
-                                h_out.data_ptr(), y_out.data_ptr(), rows, n,
-                                stream)
+    _rows_inputs([("h_out", h_out), ("y_out", y_out)], [], a)
+    with torch.cuda.device(a.device):
+        if a.dtype == torch.float32:
+            rc = _lib.sandwich_tail(a.data_ptr(), r.data_ptr(),
+                                    gamma_post.data_ptr(), float(eps_post),
+                                    gamma_pre.data_ptr(), float(eps_pre),
+                                    h_out.data_ptr(), y_out.data_ptr(), rows,
+                                    n, _stream(a.device))
+        else:
+            rc = _lib.sandwich_tail_typed(
+                a.data_ptr(), r.data_ptr(), gamma_post.data_ptr(),
+                float(eps_post), gamma_pre.data_ptr(), float(eps_pre),
+                h_out.data_ptr(), y_out.data_ptr(), rows, n, _dtype_code(a),
+                _stream(a.device))
     _lib.check(rc, "sandwich_tail")
     return h_out, y_out
+
+
+def sandwich_tail_inplace(a, residual, gamma_post, eps_post: float,
+                          gamma_pre, eps_pre: float, y_out=None):
+    """The tail with the residual stream updated in place:
+    residual += post-norm(a); returns y, the pre-norm of the updated
+    residual."""
+    torch = _torch()
+    rows, n = _rows_inputs([("a", a), ("residual", residual)],
+                           [("gamma_post", gamma_post),
+                            ("gamma_pre", gamma_pre)], a)
+    y_out = torch.empty_like(a) if y_out is None else y_out
+    _rows_inputs([("y_out", y_out)], [], a)
+    with torch.cuda.device(a.device):
+        rc = _lib.sandwich_tail_inplace(
+            a.data_ptr(), residual.data_ptr(), gamma_post.data_ptr(),
+            float(eps_post), gamma_pre.data_ptr(), float(eps_pre),
+            y_out.data_ptr(), rows, n, _dtype_code(a), _stream(a.device))
+    _lib.check(rc, "sandwich_tail_inplace")
+    return y_out
+
+
+def norm_then_add(a, r, gamma, eps: float, out_scale=None, out=None):
+    """out = (a / sqrt(mean(a^2) + eps) * gamma + r) * out_scale[0].
+
+    out_scale: None, or a one-element float32 GPU tensor (read on the GPU).
+    ``out is r`` updates the residual in place."""
+    torch = _torch()
+    rows, n = _rows_inputs([("a", a), ("r", r)], [("gamma", gamma)], a)
+    out = torch.empty_like(a) if out is None else out
+    _rows_inputs([("out", out)], [], a)
+    scale_ptr = None
+    if out_scale is not None:
+        _check_tensor("out_scale", out_scale, a.device, torch.float32)
+        if out_scale.numel() < 1:
+            raise ValueError("out_scale must hold one element")
+        scale_ptr = out_scale.data_ptr()
+    with torch.cuda.device(a.device):
+        rc = _lib.norm_then_add(a.data_ptr(), r.data_ptr(), gamma.data_ptr(),
+                                float(eps), scale_ptr, out.data_ptr(), rows,
+                                n, _dtype_code(a), _stream(a.device))
+    _lib.check(rc, "norm_then_add")
+    return out
+
+
+def add_then_norm(a, b, gamma, eps: float, sum_out=None, y_out=None):
+    """s = a + b; y = s / sqrt(mean(s^2) + eps) * gamma. Returns (s, y).
+    ``sum_out`` may be ``a`` or ``b`` (accumulate in place)."""
+    torch = _torch()
+    rows, n = _rows_inputs([("a", a), ("b", b)], [("gamma", gamma)], a)
+    sum_out = torch.empty_like(a) if sum_out is None else sum_out
+    y_out = torch.empty_like(a) if y_out is None else y_out
+    _rows_inputs([("sum_out", sum_out), ("y_out", y_out)], [], a)
+    with torch.cuda.device(a.device):
+        rc = _lib.add_then_norm(a.data_ptr(), b.data_ptr(), gamma.data_ptr(),
+                                float(eps), sum_out.data_ptr(),
+                                y_out.data_ptr(), rows, n, _dtype_code(a),
+                                _stream(a.device))
+    _lib.check(rc, "add_then_norm")
+    return sum_out, y_out
 
 
 @contextlib.contextmanager

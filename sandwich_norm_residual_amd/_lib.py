@@ -14,6 +14,7 @@ LIBRARY = os.path.join(PKG, "libsnr.so")
 
 SNR_F32 = 0
 SNR_BF16 = 1
+SNR_F16 = 2
 
 SNR_OK = 0
 SNR_ERR_NULL = 1
@@ -40,6 +41,14 @@ SIGNATURES = {
     "rmsnorm_fwd": (_int, [_vp, _vp, _f, _i64, _i64, _int, _vp, _vp]),
     "sandwich_tail": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp, _i64,
                              _i64, _vp]),
+    "sandwich_tail_typed": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp,
+                                   _i64, _i64, _int, _vp]),
+    "sandwich_tail_inplace": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _i64,
+                                     _i64, _int, _vp]),
+    "norm_then_add": (_int, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _int,
+                             _vp]),
+    "add_then_norm": (_int, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _int,
+                             _vp]),
     "snr_strerror": (ctypes.c_char_p, [_int]),
     "snr_last_hip_error": (_int, []),
     "snr_force_shape": (_int, [_int, _int, _int]),
@@ -97,6 +106,32 @@ def sandwich_tail(a: int, r: int, gamma_post: int, eps_post: float,
     """Raw call with integer device addresses; returns the SNR_* code."""
     return lib().sandwich_tail(a, r, gamma_post, eps_post, gamma_pre, eps_pre,
                                h_out, y_out, rows, n, stream)
+
+
+def sandwich_tail_typed(a, r, gamma_post, eps_post, gamma_pre, eps_pre,
+                        h_out, y_out, rows, n, dtype, stream) -> int:
+    return lib().sandwich_tail_typed(a, r, gamma_post, eps_post, gamma_pre,
+                                     eps_pre, h_out, y_out, rows, n, dtype,
+                                     stream)
+
+
+def sandwich_tail_inplace(a, residual, gamma_post, eps_post, gamma_pre,
+                          eps_pre, y_out, rows, n, dtype, stream) -> int:
+    return lib().sandwich_tail_inplace(a, residual, gamma_post, eps_post,
+                                       gamma_pre, eps_pre, y_out, rows, n,
+                                       dtype, stream)
+
+
+def norm_then_add(a, r, gamma, eps, out_scale, out, rows, n, dtype,
+                  stream) -> int:
+    return lib().norm_then_add(a, r, gamma, eps, out_scale, out, rows, n,
+                               dtype, stream)
+
+
+def add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n, dtype,
+                  stream) -> int:
+    return lib().add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n,
+                               dtype, stream)
 
 
 def force_shape(kind: int, g: int = 0, vpt: int = 0) -> None:

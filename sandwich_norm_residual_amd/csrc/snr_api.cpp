@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -322,53 +323,44 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     return SNR_OK;
 }
 
-}  // namespace
-}  // namespace snr
-
-using namespace snr;
-
-extern "C" {
-
-int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
-                int64_t n, int dtype, void *y, hipStream_t stream) {
-    if (dtype != SNR_F32 && dtype != SNR_BF16) return SNR_ERR_DTYPE;
-    const int64_t es = dtype == SNR_F32 ? 4 : 2;
-    int rc = check_shape(rows, n, es);
-    if (rc != SNR_OK) return rc;
-    if (!eps_ok(eps)) return SNR_ERR_EPS;
-    if (rows == 0) return SNR_OK;
-    if (!x || !gamma || !y) return SNR_ERR_NULL;
-    if (!aligned(x, es) || !aligned(gamma, es) || !aligned(y, es))
-        return SNR_ERR_ALIGN;
-    const int64_t tb = rows * n * es, gb = n * es;
-    if (y != x && overlaps(y, tb, x, tb)) return SNR_ERR_ALIAS;
-    if (overlaps(y, tb, gamma, gb)) return SNR_ERR_ALIAS;
-
-    RowArgs a{};
-    a.x0 = x;
-    a.g0 = gamma;
-    a.out0 = y;
-    a.eps0 = eps;
-    a.rows = rows;
-    a.n = (int32_t)n;
-    return launch(OP_PLAIN, dtype == SNR_F32 ? ST_F32 : ST_BF16, es, a,
-                  stream);
+// Storage of a dtype code and its element size (0 when the code is invalid).
+int storage_of(int dtype, int64_t *esize) {
+    switch (dtype) {
+    case SNR_F32: *esize = 4; return ST_F32;
+    case SNR_BF16: *esize = 2; return ST_BF16;
+    case SNR_F16: *esize = 2; return ST_F16;
+    default: *esize = 0; return -1;
+    }
 }
 
-int sandwich_tail(const float *a, const float *r, const float *gamma_post,
-                  float eps_post, const float *gamma_pre, float eps_pre,
-                  float *h_out, float *y_out, int64_t rows, int64_t n,
-                  hipStream_t stream) {
-    int rc = check_shape(rows, n, 4);
+// Common front of the two-input operations: shape, epsilons, nulls,
+// element alignment. Returns SNR_OK, an error, or -1 for "rows == 0, done".
+int check_common(int64_t rows, int64_t n, int64_t es,
+                 std::initializer_list<float> eps,
+                 std::initializer_list<const void *> ptrs) {
+    int rc = check_shape(rows, n, es);
     if (rc != SNR_OK) return rc;
-    if (!eps_ok(eps_post) || !eps_ok(eps_pre)) return SNR_ERR_EPS;
-    if (rows == 0) return SNR_OK;
-    if (!a || !r || !gamma_post || !gamma_pre || !h_out || !y_out)
-        return SNR_ERR_NULL;
-    const void *ptrs[] = {a, r, gamma_post, gamma_pre, h_out, y_out};
+    for (float e : eps)
+        if (!eps_ok(e)) return SNR_ERR_EPS;
+    if (rows == 0) return -1;
     for (const void *p : ptrs)
-        if (!aligned(p, 4)) return SNR_ERR_ALIGN;
-    const int64_t tb = rows * n * 4, gb = n * 4;
+        if (!p) return SNR_ERR_NULL;
+    for (const void *p : ptrs)
+        if (!aligned(p, (uintptr_t)es)) return SNR_ERR_ALIGN;
+    return SNR_OK;
+}
+
+int tail_impl(const void *a, const void *r, const void *gamma_post,
+              float eps_post, const void *gamma_pre, float eps_pre,
+              void *h_out, void *y_out, int64_t rows, int64_t n, int dtype,
+              hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    int rc = check_common(rows, n, es, {eps_post, eps_pre},
+                          {a, r, gamma_post, gamma_pre, h_out, y_out});
+    if (rc != SNR_OK) return rc < 0 ? SNR_OK : rc;
+    const int64_t tb = rows * n * es, gb = n * es;
     // y_out may overlap nothing; h_out may only coincide exactly with r.
     if (overlaps(y_out, tb, a, tb) || overlaps(y_out, tb, r, tb) ||
         overlaps(y_out, tb, h_out, tb) || overlaps(y_out, tb, gamma_post, gb) ||
@@ -390,7 +382,117 @@ int sandwich_tail(const float *a, const float *r, const float *gamma_post,
     args.eps1 = eps_pre;
     args.rows = rows;
     args.n = (int32_t)n;
-    return launch(OP_TAIL, ST_F32, 4, args, stream);
+    return launch(OP_TAIL, st, es, args, stream);
+}
+
+}  // namespace
+}  // namespace snr
+
+using namespace snr;
+
+extern "C" {
+
+int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
+                int64_t n, int dtype, void *y, hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    int rc = check_common(rows, n, es, {eps}, {x, gamma, y});
+    if (rc != SNR_OK) return rc < 0 ? SNR_OK : rc;
+    const int64_t tb = rows * n * es, gb = n * es;
+    if (y != x && overlaps(y, tb, x, tb)) return SNR_ERR_ALIAS;
+    if (overlaps(y, tb, gamma, gb)) return SNR_ERR_ALIAS;
+
+    RowArgs a{};
+    a.x0 = x;
+    a.g0 = gamma;
+    a.out0 = y;
+    a.eps0 = eps;
+    a.rows = rows;
+    a.n = (int32_t)n;
+    return launch(OP_PLAIN, st, es, a, stream);
+}
+
+int sandwich_tail(const float *a, const float *r, const float *gamma_post,
+                  float eps_post, const float *gamma_pre, float eps_pre,
+                  float *h_out, float *y_out, int64_t rows, int64_t n,
+                  hipStream_t stream) {
+    return tail_impl(a, r, gamma_post, eps_post, gamma_pre, eps_pre, h_out,
+                     y_out, rows, n, SNR_F32, stream);
+}
+
+int sandwich_tail_typed(const void *a, const void *r, const void *gamma_post,
+                        float eps_post, const void *gamma_pre, float eps_pre,
+                        void *h_out, void *y_out, int64_t rows, int64_t n,
+                        int dtype, hipStream_t stream) {
+    return tail_impl(a, r, gamma_post, eps_post, gamma_pre, eps_pre, h_out,
+                     y_out, rows, n, dtype, stream);
+}
+
+int sandwich_tail_inplace(const void *a, void *residual,
+                          const void *gamma_post, float eps_post,
+                          const void *gamma_pre, float eps_pre, void *y_out,
+                          int64_t rows, int64_t n, int dtype,
+                          hipStream_t stream) {
+    return tail_impl(a, residual, gamma_post, eps_post, gamma_pre, eps_pre,
+                     residual, y_out, rows, n, dtype, stream);
+}
+
+int norm_then_add(const void *a, const void *r, const void *gamma, float eps,
+                  const float *out_scale, void *out, int64_t rows, int64_t n,
+                  int dtype, hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    int rc = check_common(rows, n, es, {eps}, {a, r, gamma, out});
+    if (rc != SNR_OK) return rc < 0 ? SNR_OK : rc;
+    if (out_scale && !aligned(out_scale, 4)) return SNR_ERR_ALIGN;
+    const int64_t tb = rows * n * es, gb = n * es;
+    // out may coincide exactly with r (the residual updated in place).
+    if (overlaps(out, tb, a, tb) || overlaps(out, tb, gamma, gb) ||
+        overlaps(out, tb, out_scale, 4))
+        return SNR_ERR_ALIAS;
+    if (out != r && overlaps(out, tb, r, tb)) return SNR_ERR_ALIAS;
+
+    RowArgs args{};
+    args.x0 = a;
+    args.x1 = r;
+    args.g0 = gamma;
+    args.out0 = out;
+    args.scale = out_scale;
+    args.eps0 = eps;
+    args.rows = rows;
+    args.n = (int32_t)n;
+    return launch(OP_NORM_ADD, st, es, args, stream);
+}
+
+int add_then_norm(const void *a, const void *b, const void *gamma, float eps,
+                  void *sum_out, void *y_out, int64_t rows, int64_t n,
+                  int dtype, hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    int rc = check_common(rows, n, es, {eps}, {a, b, gamma, sum_out, y_out});
+    if (rc != SNR_OK) return rc < 0 ? SNR_OK : rc;
+    const int64_t tb = rows * n * es, gb = n * es;
+    if (overlaps(y_out, tb, a, tb) || overlaps(y_out, tb, b, tb) ||
+        overlaps(y_out, tb, sum_out, tb) || overlaps(y_out, tb, gamma, gb))
+        return SNR_ERR_ALIAS;
+    // sum_out may coincide exactly with a or with b.
+    if (overlaps(sum_out, tb, gamma, gb)) return SNR_ERR_ALIAS;
+    if (sum_out != a && overlaps(sum_out, tb, a, tb)) return SNR_ERR_ALIAS;
+    if (sum_out != b && overlaps(sum_out, tb, b, tb)) return SNR_ERR_ALIAS;
+
+    RowArgs args{};
+    args.x0 = a;
+    args.x1 = b;
+    args.g0 = gamma;
+    args.out0 = sum_out;
+    args.out1 = y_out;
+    args.eps0 = eps;
+    args.rows = rows;
+    args.n = (int32_t)n;
+    return launch(OP_ADD_NORM, st, es, args, stream);
 }
 
 const char *snr_strerror(int code) {
@@ -400,7 +502,7 @@ const char *snr_strerror(int code) {
     case SNR_ERR_SHAPE:
         return "invalid shape (n < 1, n > 2^31-1, rows < 0, size overflow, "
                "or a forced dispatch shape that cannot hold the row)";
-    case SNR_ERR_DTYPE: return "unsupported dtype";
+    case SNR_ERR_DTYPE: return "unsupported dtype (SNR_F32, SNR_BF16 or SNR_F16)";
     case SNR_ERR_EPS: return "epsilon must be finite and > 0";
     case SNR_ERR_ALIAS: return "output buffers overlap inputs or each other";
     case SNR_ERR_ALIGN: return "pointer not aligned to its element size";

@@ -7,13 +7,17 @@
 
 namespace snr {
 
-enum Op : int { OP_PLAIN = 0, OP_TAIL = 1 };
-enum Storage : int { ST_F32 = 0, ST_BF16 = 1 };
+enum Op : int { OP_PLAIN = 0, OP_TAIL = 1, OP_NORM_ADD = 2, OP_ADD_NORM = 3 };
+enum Storage : int { ST_F32 = 0, ST_BF16 = 1, ST_F16 = 2 };
 enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2, KIND_MULTIPASS = 3 };
 
-// Everything a row kernel needs. For OP_PLAIN only x0, g0, out0 and eps0 are
-// used; for OP_TAIL: x0 = a, x1 = r, g0 = gamma_post, g1 = gamma_pre,
-// out0 = h, out1 = y, eps0 = eps_post, eps1 = eps_pre.
+// Everything a row kernel needs.
+//   OP_PLAIN:    x0 = x, g0 = gamma, out0 = y, eps0
+//   OP_TAIL:     x0 = a, x1 = r, g0 = gamma_post, g1 = gamma_pre, out0 = h,
+//                out1 = y, eps0 = eps_post, eps1 = eps_pre
+//   OP_NORM_ADD: x0 = a, x1 = r, g0 = gamma, out0 = out, eps0, scale (device
+//                pointer to one f32, or null for 1)
+//   OP_ADD_NORM: x0 = a, x1 = b, g0 = gamma, out0 = s, out1 = y, eps0
 struct RowArgs {
     const void *x0;
     const void *x1;
@@ -21,6 +25,7 @@ struct RowArgs {
     const void *g1;
     void *out0;
     void *out1;
+    const float *scale;
     float eps0;
     float eps1;
     int64_t rows;  // rows in the whole tensor
@@ -63,7 +68,7 @@ constexpr int kMultiVpt = 8;
 struct KernelEntry {
     int op;        // Op
     int storage;   // Storage
-    int width;     // elements per 128-bit vector (4 f32, 8 bf16)
+    int width;     // elements per 128-bit vector (4 f32, 8 bf16/f16)
     int kind;      // Kind
     int g;         // lanes per row (rowtile) / workgroup size (split)
     int vpt;       // loads held per lane

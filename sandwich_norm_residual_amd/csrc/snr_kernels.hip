@@ -1,18 +1,25 @@
-// snr_kernels.hip - gfx950 (CDNA4) kernels for row-wise RMSNorm and the fused
-// dual-epsilon sandwich tail.
+// snr_kernels.hip - gfx950 (CDNA4) kernels for row-wise RMSNorm, the fused
+// dual-epsilon sandwich tail, and the tail's two halves.
 //
 // What is computed ("RMSNorm and the dual-epsilon sandwich", Muser book
-// chapter 12):
-//   plain (section 12.1):  y = x / sqrt(mean(x^2) + eps) * gamma
-//   tail (sections 12.2 and 12.4.3):
+// chapter 12, and Hesper's "RMSNorm Layer" page):
+//   plain (Muser 12.1):      y = x / sqrt(mean(x^2) + eps) * gamma
+//   tail (Muser 12.2, 12.4.3):
 //       h = r + a / sqrt(mean(a^2) + eps_post) * gamma_post
 //       y = h / sqrt(mean(h^2) + eps_pre) * gamma_pre
+//   norm_then_add (Hesper rmsNormThenAdd[ThenBroadcastScale]Kernel):
+//       out = (a / sqrt(mean(a^2) + eps) * gamma + r) * scale
+//   add_then_norm (Hesper residualAddRmsNormKernel):
+//       s = a + b;  y = s / sqrt(mean(s^2) + eps) * gamma   (writes s and y)
+// An intermediate that a later norm reads (the tail's h, add_then_norm's s)
+// is normalised as it is stored: rounded to the storage type first (the
+// identity for f32).
 //
 // Design (HBM-bound, no contraction, so no MFMA):
 // * Each row is read from HBM exactly once: every lane loads its share of the
 //   row into registers with coalesced 128-bit loads (the n % W elements past
-//   the last whole vector one at a time), the sum of squares is reduced, and the
-//   normalise pass works from those registers. The tail also keeps h in
+//   the last whole vector one at a time), the sum of squares is reduced, and
+//   the normalise pass works from those registers. The tail also keeps h in
 //   registers for its second reduction, so a and r are read once and h and y
 //   written once.
 // * Sums of squares accumulate in f32. Inside a wavefront the reduction uses
@@ -31,6 +38,8 @@
 //   x `chunks` workgroups; workgroup (g, c) handles chunk c of rows g,
 //   g + groups, g + 2 groups, ... in order, so a wait only ever depends on
 //   resident workgroups that are working on the same row.
+// * Multi-pass kernels for rows so wide that their chunks cannot all be
+//   co-resident: partial sums through device memory (rows read twice).
 // * Stores of outputs and loads of row data are non-temporal (each byte is
 //   touched once); gains use ordinary cached loads (every row re-reads them).
 #include <hip/hip_runtime.h>
@@ -43,11 +52,12 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Storage codecs. Rows are moved with 128-bit accesses: W elements per
-// vector (4 f32 or 8 bf16). The vector types carry only element alignment:
-// gfx950 performs dwordx4 accesses at any 4-byte (f32) or 2-byte (bf16)
-// boundary, so rows whose start is not 16-byte aligned (odd n, offset views)
-// still use 128-bit accesses. The n % W elements after a row's last whole
-// vector are moved one at a time.
+// vector (4 f32, or 8 bf16/f16). The vector types carry only element
+// alignment: gfx950 performs dwordx4 accesses at any 4-byte (f32) or 2-byte
+// (16-bit types) boundary, so rows whose start is not 16-byte aligned (odd
+// n, offset views) still use 128-bit accesses. The n % W elements after a
+// row's last whole vector are moved one at a time.
+// `round` rounds an f32 value to the storage type and back (exact decode).
 // ---------------------------------------------------------------------------
 template <int ST>
 struct Codec;
@@ -77,33 +87,67 @@ struct Codec<ST_F32> {
     __device__ static void store1_nt(T *row, int j, float v) {
         __builtin_nontemporal_store(v, row + j);
     }
+    __device__ static float round(float v) { return v; }
 };
+
+// Two 16-bit values per 32-bit word, element 2k in the low half.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // bf16 -> f32 is exact (a bf16 is the upper half of an f32); f32 -> bf16
 // rounds to nearest even (gfx950's v_cvt_pk_bf16_f32).
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float bf16_lo(unsigned int w) {
-    return __uint_as_float(w << 16);
-}
-__device__ __forceinline__ float bf16_hi(unsigned int w) {
-    return __uint_as_float(w & 0xFFFF0000u);
-}
-__device__ __forceinline__ unsigned int bf16_pack(float lo, float hi) {
-    const f32x2 f = {lo, hi};
-    return __builtin_bit_cast(unsigned int, __builtin_convertvector(f, bf16x2));
-}
+struct BF16Bits {
+    __device__ static float lo(unsigned int w) {
+        return __uint_as_float(w << 16);
+    }
+    __device__ static float hi(unsigned int w) {
+        return __uint_as_float(w & 0xFFFF0000u);
+    }
+    __device__ static unsigned int pack(float a, float b) {
+        const f32x2 f = {a, b};
+        return __builtin_bit_cast(unsigned int,
+                                  __builtin_convertvector(f, bf16x2));
+    }
+    __device__ static float one(unsigned short b) {
+        return __uint_as_float((unsigned int)b << 16);
+    }
+    __device__ static unsigned short enc(float v) {
+        return __builtin_bit_cast(unsigned short, (__bf16)v);
+    }
+};
 
-template <>
-struct Codec<ST_BF16> {
+// f16 -> f32 is exact; f32 -> f16 rounds to nearest even.
+struct F16Bits {
+    __device__ static float lo(unsigned int w) {
+        return (float)__builtin_bit_cast(f16x2, w).x;
+    }
+    __device__ static float hi(unsigned int w) {
+        return (float)__builtin_bit_cast(f16x2, w).y;
+    }
+    __device__ static unsigned int pack(float a, float b) {
+        const f32x2 f = {a, b};
+        return __builtin_bit_cast(unsigned int,
+                                  __builtin_convertvector(f, f16x2));
+    }
+    __device__ static float one(unsigned short b) {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+    __device__ static unsigned short enc(float v) {
+        return __builtin_bit_cast(unsigned short, (_Float16)v);
+    }
+};
+
+template <class B>
+struct Codec16 {
     using T = unsigned short;
     static constexpr int W = 8;
     typedef unsigned int vec __attribute__((ext_vector_type(4), aligned(2)));
     __device__ static void unpack(const vec q, float (&v)[8]) {
-        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
-        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
-        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+        v[0] = B::lo(q.x); v[1] = B::hi(q.x);
+        v[2] = B::lo(q.y); v[3] = B::hi(q.y);
+        v[4] = B::lo(q.z); v[5] = B::hi(q.z);
+        v[6] = B::lo(q.w); v[7] = B::hi(q.w);
     }
     __device__ static void load_nt(const T *row, int i, float (&v)[8]) {
         unpack(__builtin_nontemporal_load(reinterpret_cast<const vec *>(row) + i),
@@ -113,22 +157,26 @@ struct Codec<ST_BF16> {
         unpack(reinterpret_cast<const vec *>(base)[i], v);
     }
     __device__ static void store_nt(T *row, int i, const float (&v)[8]) {
-        const vec q = {bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3]),
-                       bf16_pack(v[4], v[5]), bf16_pack(v[6], v[7])};
+        const vec q = {B::pack(v[0], v[1]), B::pack(v[2], v[3]),
+                       B::pack(v[4], v[5]), B::pack(v[6], v[7])};
         __builtin_nontemporal_store(q, reinterpret_cast<vec *>(row) + i);
     }
     __device__ static float load1_nt(const T *row, int j) {
-        return __uint_as_float((unsigned int)__builtin_nontemporal_load(row + j)
-                               << 16);
+        return B::one(__builtin_nontemporal_load(row + j));
     }
     __device__ static float load1(const T *base, int j) {
-        return __uint_as_float((unsigned int)base[j] << 16);
+        return B::one(base[j]);
     }
     __device__ static void store1_nt(T *row, int j, float v) {
-        __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, (__bf16)v),
-                                    row + j);
+        __builtin_nontemporal_store(B::enc(v), row + j);
     }
+    __device__ static float round(float v) { return B::one(B::enc(v)); }
 };
+
+template <>
+struct Codec<ST_BF16> : Codec16<BF16Bits> {};
+template <>
+struct Codec<ST_F16> : Codec16<F16Bits> {};
 
 // ---------------------------------------------------------------------------
 // Reductions
@@ -180,19 +228,15 @@ __device__ __forceinline__ float row_total(float s, float *slot) {
 
 template <int W>
 __device__ __forceinline__ float sumsq(const float (&v)[W]) {
-    if constexpr (W == 1) {
-        return v[0] * v[0];
-    } else {
-        float p[W / 2];
+    float p[W / 2];
 #pragma unroll
-        for (int e = 0; e < W / 2; ++e)
-            p[e] = fmaf(v[2 * e], v[2 * e], v[2 * e + 1] * v[2 * e + 1]);
+    for (int e = 0; e < W / 2; ++e)
+        p[e] = fmaf(v[2 * e], v[2 * e], v[2 * e + 1] * v[2 * e + 1]);
 #pragma unroll
-        for (int w = W / 4; w >= 1; w /= 2)
+    for (int w = W / 4; w >= 1; w /= 2)
 #pragma unroll
-            for (int e = 0; e < w; ++e) p[e] += p[e + w];
-        return p[0];
-    }
+        for (int e = 0; e < w; ++e) p[e] += p[e + w];
+    return p[0];
 }
 
 __device__ __forceinline__ float inv_rms(float total, int n, float eps) {
@@ -207,7 +251,7 @@ __device__ __forceinline__ void zero(float (&v)[W]) {
 }
 
 // ---------------------------------------------------------------------------
-// One row (or one chunk of a row), shared by both kernels.
+// One row (or one chunk of a row), shared by the row-tile and split kernels.
 //
 // The lane holds vectors vbase + k*vstride (k < VPT) of the row and, when
 // `sown`, the remainder elements sbase + q*sstride (q < EX) that follow the
@@ -215,10 +259,9 @@ __device__ __forceinline__ void zero(float (&v)[W]) {
 // squares into the row total (which = 0 for the first norm, 1 for the
 // second); every lane of the row must call it.
 //
-// Plain:  y = x * (1/sqrt(sum/n + eps0)) * g0
-// Tail:   h = r + a * (1/sqrt(sum_a/n + eps0)) * g0;  y = h * (1/sqrt(sum_h/n
-//         + eps1)) * g1, with h kept in registers between the two norms.
-// LATE (tail only) loads r while forming h instead of with a.
+// LATE (tail and norm_then_add): r is loaded while forming the output
+// instead of together with a, so only one row stream is held in registers.
+// add_then_norm always holds only the sum s = a + b.
 // ---------------------------------------------------------------------------
 template <int OP, int ST, int VPT, int EX, bool LATE, class Reduce>
 __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
@@ -228,7 +271,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
     using C = Codec<ST>;
     using T = typename C::T;
     constexpr int W = C::W;
-    constexpr bool HOLD_R = OP == OP_TAIL && !LATE;
+    constexpr bool HOLD_R = (OP == OP_TAIL || OP == OP_NORM_ADD) && !LATE;
     const int nv = p.nv;
     const int rem = p.rem;
     const int tail0 = nv * W;  // first remainder element of the row
@@ -240,6 +283,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
 
     const T *x0 = static_cast<const T *>(p.x0) + off;
     const T *x1 = static_cast<const T *>(p.x1) + off;
+    (void)x1;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int i = vbase + k * vstride;
@@ -263,6 +307,29 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                                               : 0.0f;
         }
     }
+    T *out0 = static_cast<T *>(p.out0) + off;
+    if constexpr (OP == OP_ADD_NORM) {
+        // s = a + b, rounded to storage, stored, and kept for the norm.
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int i = vbase + k * vstride;
+            if (live && i < nv) {
+                float b[W];
+                C::load_nt(x1, i, b);
+#pragma unroll
+                for (int e = 0; e < W; ++e) v0[k][e] = C::round(v0[k][e] + b[e]);
+                C::store_nt(out0, i, v0[k]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EX; ++q) {
+            const int j = sbase + q * sstride;
+            if (live && sown && j < rem) {
+                e0[q] = C::round(e0[q] + C::load1_nt(x1, tail0 + j));
+                C::store1_nt(out0, tail0 + j, e0[q]);
+            }
+        }
+    }
 
     float s = 0.0f;
 #pragma unroll
@@ -270,10 +337,11 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
 #pragma unroll
     for (int q = 0; q < EX; ++q) s = fmaf(e0[q], e0[q], s);
     const float inv0 = inv_rms(reduce(s, 0), p.n, p.eps0);
-
     const T *g0 = static_cast<const T *>(p.g0);
-    T *out0 = static_cast<T *>(p.out0) + off;
-    if constexpr (OP == OP_PLAIN) {
+
+    if constexpr (OP == OP_PLAIN || OP == OP_ADD_NORM) {
+        // y = x * inv * gamma (add_then_norm: x is the stored sum)
+        T *y = static_cast<T *>(OP == OP_PLAIN ? p.out0 : p.out1) + off;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int i = vbase + k * vstride;
@@ -282,18 +350,20 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                 C::load(g0, i, g);
 #pragma unroll
                 for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
-                C::store_nt(out0, i, o);
+                C::store_nt(y, i, o);
             }
         }
 #pragma unroll
         for (int q = 0; q < EX; ++q) {
             const int j = sbase + q * sstride;
             if (live && sown && j < rem)
-                C::store1_nt(out0, tail0 + j,
+                C::store1_nt(y, tail0 + j,
                              e0[q] * inv0 * C::load1(g0, tail0 + j));
         }
     } else {
-        // h lives in v1/e1, or in v0/e0 once a is consumed when r is late.
+        // h = r + a * inv * gamma0, kept in registers (v1/e1, or v0/e0 once
+        // a is consumed when r is late). norm_then_add stores h * scale.
+        const float scale = (OP == OP_NORM_ADD && p.scale) ? *p.scale : 1.0f;
         float(*hv)[W] = LATE ? v0 : v1;
         float *he = LATE ? e0 : e1;
 #pragma unroll
@@ -308,10 +378,18 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
 #pragma unroll
                     for (int e = 0; e < W; ++e) rr[e] = v1[k][e];
                 }
+                if constexpr (OP == OP_TAIL) {
 #pragma unroll
-                for (int e = 0; e < W; ++e)
-                    hv[k][e] = fmaf(v0[k][e] * inv0, g[e], rr[e]);
-                C::store_nt(out0, i, hv[k]);
+                    for (int e = 0; e < W; ++e)
+                        hv[k][e] = C::round(fmaf(v0[k][e] * inv0, g[e], rr[e]));
+                    C::store_nt(out0, i, hv[k]);
+                } else {
+                    float o[W];
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        o[e] = fmaf(v0[k][e] * inv0, g[e], rr[e]) * scale;
+                    C::store_nt(out0, i, o);
+                }
             }
         }
 #pragma unroll
@@ -319,36 +397,44 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             const int j = sbase + q * sstride;
             if (live && sown && j < rem) {
                 const float rr = LATE ? C::load1_nt(x1, tail0 + j) : e1[q];
-                he[q] = fmaf(e0[q] * inv0, C::load1(g0, tail0 + j), rr);
-                C::store1_nt(out0, tail0 + j, he[q]);
+                const float h =
+                    fmaf(e0[q] * inv0, C::load1(g0, tail0 + j), rr);
+                if constexpr (OP == OP_TAIL) {
+                    he[q] = C::round(h);
+                    C::store1_nt(out0, tail0 + j, he[q]);
+                } else {
+                    C::store1_nt(out0, tail0 + j, h * scale);
+                }
             }
         }
-        float sh = 0.0f;
+        if constexpr (OP == OP_TAIL) {
+            float sh = 0.0f;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) sh += sumsq<W>(hv[k]);
+            for (int k = 0; k < VPT; ++k) sh += sumsq<W>(hv[k]);
 #pragma unroll
-        for (int q = 0; q < EX; ++q) sh = fmaf(he[q], he[q], sh);
-        const float inv1 = inv_rms(reduce(sh, 1), p.n, p.eps1);
+            for (int q = 0; q < EX; ++q) sh = fmaf(he[q], he[q], sh);
+            const float inv1 = inv_rms(reduce(sh, 1), p.n, p.eps1);
 
-        const T *g1 = static_cast<const T *>(p.g1);
-        T *out1 = static_cast<T *>(p.out1) + off;
+            const T *g1 = static_cast<const T *>(p.g1);
+            T *out1 = static_cast<T *>(p.out1) + off;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = vbase + k * vstride;
-            if (live && i < nv) {
-                float g[W], o[W];
-                C::load(g1, i, g);
+            for (int k = 0; k < VPT; ++k) {
+                const int i = vbase + k * vstride;
+                if (live && i < nv) {
+                    float g[W], o[W];
+                    C::load(g1, i, g);
 #pragma unroll
-                for (int e = 0; e < W; ++e) o[e] = hv[k][e] * inv1 * g[e];
-                C::store_nt(out1, i, o);
+                    for (int e = 0; e < W; ++e) o[e] = hv[k][e] * inv1 * g[e];
+                    C::store_nt(out1, i, o);
+                }
             }
-        }
 #pragma unroll
-        for (int q = 0; q < EX; ++q) {
-            const int j = sbase + q * sstride;
-            if (live && sown && j < rem)
-                C::store1_nt(out1, tail0 + j,
-                             he[q] * inv1 * C::load1(g1, tail0 + j));
+            for (int q = 0; q < EX; ++q) {
+                const int j = sbase + q * sstride;
+                if (live && sown && j < rem)
+                    C::store1_nt(out1, tail0 + j,
+                                 he[q] * inv1 * C::load1(g1, tail0 + j));
+            }
         }
     }
 }
@@ -366,7 +452,15 @@ constexpr int rowtile_extra() {
     return (Codec<ST>::W - 1 + G - 1) / G;
 }
 
-template <int OP, int ST, int G, int VPT, bool LATE = false>
+// r is loaded late where holding two row streams would not fit the 128
+// registers a lane of a 1024-lane workgroup may use.
+template <int OP, int ST, int G, int VPT>
+constexpr bool rowtile_late() {
+    return (OP == OP_TAIL || OP == OP_NORM_ADD) && G == 1024 &&
+           VPT * Codec<ST>::W >= 64;
+}
+
+template <int OP, int ST, int G, int VPT>
 __global__ void __launch_bounds__(rowtile_block<G>())
 rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     constexpr int BLOCK = rowtile_block<G>();
@@ -378,7 +472,8 @@ rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     const int64_t row = row0 + (int64_t)blockIdx.x * RPB + threadIdx.x / G;
     const bool live = row < row_end;
     const int64_t off = live ? row * (int64_t)p.n : 0;
-    process_row<OP, ST, VPT, rowtile_extra<ST, G>(), LATE>(
+    process_row<OP, ST, VPT, rowtile_extra<ST, G>(),
+                rowtile_late<OP, ST, G, VPT>()>(
         p, off, live, sub, G, sub, G, true,
         [&](float s, int which) { return row_total<G>(s, red[which]); });
 }
@@ -482,12 +577,14 @@ split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
 // co-resident workgroups). Each pass is a plain grid; partial sums go
 // through device memory and are added in chunk order, so results stay
 // deterministic. These passes read a row more than once:
-//   plain: partial(x) -> combine -> y = x * inv * g                  (x twice)
-//   tail:  partial(a) -> combine -> h = r + a*inv_a*gp, partial(h) ->
-//          combine -> y = h * inv_h * gq                      (a and h twice)
+//   plain:         partial(x) -> combine -> y = x * inv * g          (x twice)
+//   tail:          partial(a) -> combine -> h = r + a*inv*gp, partial(h)
+//                  -> combine -> y = h * inv_h * gq          (a and h twice)
+//   norm_then_add: partial(a) -> combine -> out = (a*inv*g + r) * scale
+//   add_then_norm: s = a + b, partial(s) -> combine -> y = s * inv * g
 // ---------------------------------------------------------------------------
-constexpr int MB = 256;           // threads per workgroup
-constexpr int MVPT = 8;           // vectors per thread per chunk
+constexpr int MB = kMultiBlock;   // threads per workgroup
+constexpr int MVPT = kMultiVpt;   // vectors per thread per chunk
 
 // Lane-strided chunk walk: vectors c*MB*MVPT + k*MB + tid, and in the last
 // chunk the remainder element tid.
@@ -537,7 +634,7 @@ pass_combine(const float *part, int chunks, int n, float eps, float *inv) {
     if (threadIdx.x == 0) inv[rl] = inv_rms(t, n, eps);
 }
 
-// plain: y = x * inv * g.
+// dst = src * inv * gain.
 template <int ST>
 __global__ void __launch_bounds__(MB)
 pass_scale(RowArgs p, const void *src, const void *gain, void *dst,
@@ -565,43 +662,56 @@ pass_scale(RowArgs p, const void *src, const void *gain, void *dst,
         [&](int j) { C::store1_nt(y, j, C::load1_nt(x, j) * r * C::load1(g, j)); });
 }
 
-// tail: h = r + a * inv_a * gamma_post, stored, with its chunk's sum of
-// squares in part[rl * chunks + c].
+// The elementwise middle pass, with the chunk's sum of squares of what it
+// stores in part[rl * chunks + c] when a later norm needs it:
+//   tail:          h = round(r + a * inv * gamma0)                 (+ part)
+//   norm_then_add: out = (a * inv * gamma0 + r) * scale
+//   add_then_norm: s = round(a + b)                                (+ part)
+template <int OP, int ST>
 __global__ void __launch_bounds__(MB)
-pass_residual(RowArgs p, int64_t row0, int chunks, const float *inv,
-              float *part) {
-    using C = Codec<ST_F32>;
+pass_fuse(RowArgs p, int64_t row0, int chunks, const float *inv, float *part) {
+    using C = Codec<ST>;
+    using T = typename C::T;
     constexpr int W = C::W;
     __shared__ float red[MB / 64];
     const int chunk = (int)(blockIdx.x % (unsigned)chunks);
     const int64_t rl = blockIdx.x / (unsigned)chunks;
     const int64_t off = (row0 + rl) * (int64_t)p.n;
-    const float *a = static_cast<const float *>(p.x0) + off;
-    const float *r = static_cast<const float *>(p.x1) + off;
-    const float *g = static_cast<const float *>(p.g0);
-    float *h = static_cast<float *>(p.out0) + off;
-    const float ia = inv[rl];
+    const T *a = static_cast<const T *>(p.x0) + off;
+    const T *r = static_cast<const T *>(p.x1) + off;
+    const T *g = static_cast<const T *>(p.g0);
+    T *o = static_cast<T *>(p.out0) + off;
+    const float ia = OP == OP_ADD_NORM ? 0.0f : inv[rl];
+    const float scale = (OP == OP_NORM_ADD && p.scale) ? *p.scale : 1.0f;
+    auto fuse = [&](float av, float rv, float gv) {
+        if constexpr (OP == OP_ADD_NORM) return C::round(av + rv);
+        else if constexpr (OP == OP_TAIL) return C::round(fmaf(av * ia, gv, rv));
+        else return fmaf(av * ia, gv, rv) * scale;
+    };
     float s = 0.0f;
-    for_chunk<ST_F32>(
+    for_chunk<ST>(
         p, chunk, chunks,
         [&](int i) {
             float av[W], rv[W], gv[W], hv[W];
             C::load_nt(a, i, av);
             C::load_nt(r, i, rv);
-            C::load(g, i, gv);
+            if constexpr (OP != OP_ADD_NORM) C::load(g, i, gv);
+            else zero(gv);
 #pragma unroll
-            for (int e = 0; e < W; ++e) hv[e] = fmaf(av[e] * ia, gv[e], rv[e]);
-            C::store_nt(h, i, hv);
+            for (int e = 0; e < W; ++e) hv[e] = fuse(av[e], rv[e], gv[e]);
+            C::store_nt(o, i, hv);
             s += sumsq<W>(hv);
         },
         [&](int j) {
-            const float hv = fmaf(C::load1_nt(a, j) * ia, C::load1(g, j),
-                                  C::load1_nt(r, j));
-            C::store1_nt(h, j, hv);
+            const float gv = OP == OP_ADD_NORM ? 0.0f : C::load1(g, j);
+            const float hv = fuse(C::load1_nt(a, j), C::load1_nt(r, j), gv);
+            C::store1_nt(o, j, hv);
             s = fmaf(hv, hv, s);
         });
-    const float t = block_total(s, red);
-    if (threadIdx.x == 0) part[rl * chunks + chunk] = t;
+    if constexpr (OP != OP_NORM_ADD) {
+        const float t = block_total(s, red);
+        if (threadIdx.x == 0) part[rl * chunks + chunk] = t;
+    }
 }
 
 __global__ void zero_kernel(unsigned int *p, int64_t words) {
@@ -614,23 +724,22 @@ __global__ void zero_kernel(unsigned int *p, int64_t words) {
 // ---------------------------------------------------------------------------
 // Launchers and the kernel table
 // ---------------------------------------------------------------------------
-template <int OP, int ST, int G, int VPT, bool LATE = false>
+template <int OP, int ST, int G, int VPT>
 hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
                           hipStream_t stream) {
     constexpr int BLOCK = rowtile_block<G>();
     constexpr int RPB = BLOCK / G;
     const int64_t blocks = (nrows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT, LATE>),
+    hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT>),
                        dim3((unsigned int)blocks), dim3(BLOCK), 0, stream, p,
                        row0, row0 + nrows);
     return hipGetLastError();
 }
 
-template <int OP, int ST, int G, int VPT, bool LATE = false>
+template <int OP, int ST, int G, int VPT>
 hipError_t occupancy_rowtile(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, rowtile_kernel<OP, ST, G, VPT, LATE>,
-        rowtile_block<G>(), 0);
+        blocks_per_cu, rowtile_kernel<OP, ST, G, VPT>, rowtile_block<G>(), 0);
 }
 
 template <int OP, int ST, int VPT>
@@ -659,22 +768,36 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
                             int64_t nrows, int chunks, hipStream_t stream) {
     float *part = scratch;
     float *inv = scratch + nrows * (int64_t)chunks;
-    const dim3 grid((unsigned int)(nrows * chunks)), rows_grid((unsigned int)nrows);
+    const dim3 grid((unsigned int)(nrows * chunks));
+    const dim3 rows_grid((unsigned int)nrows);
+    const float *cinv = inv;
+    if constexpr (OP == OP_ADD_NORM) {
+        hipLaunchKernelGGL((pass_fuse<OP, ST>), grid, dim3(MB), 0, stream, p,
+                           row0, chunks, cinv, part);
+        hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
+                           (const float *)part, chunks, p.n, p.eps0, inv);
+        hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p,
+                           (const void *)p.out0, p.g0, p.out1, row0, chunks,
+                           cinv);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(pass_sumsq<ST>, grid, dim3(MB), 0, stream, p, p.x0,
                        row0, chunks, part);
     hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
                        (const float *)part, chunks, p.n, p.eps0, inv);
     if constexpr (OP == OP_PLAIN) {
         hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p, p.x0,
-                           p.g0, p.out0, row0, chunks, (const float *)inv);
+                           p.g0, p.out0, row0, chunks, cinv);
     } else {
-        hipLaunchKernelGGL(pass_residual, grid, dim3(MB), 0, stream, p, row0,
-                           chunks, (const float *)inv, part);
-        hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
-                           (const float *)part, chunks, p.n, p.eps1, inv);
-        hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p,
-                           (const void *)p.out0, p.g1, p.out1, row0, chunks,
-                           (const float *)inv);
+        hipLaunchKernelGGL((pass_fuse<OP, ST>), grid, dim3(MB), 0, stream, p,
+                           row0, chunks, cinv, part);
+        if constexpr (OP == OP_TAIL) {
+            hipLaunchKernelGGL(pass_combine, rows_grid, dim3(MB), 0, stream,
+                               (const float *)part, chunks, p.n, p.eps1, inv);
+            hipLaunchKernelGGL(pass_scale<ST>, grid, dim3(MB), 0, stream, p,
+                               (const void *)p.out0, p.g1, p.out1, row0,
+                               chunks, cinv);
+        }
     }
     return hipGetLastError();
 }
@@ -683,38 +806,50 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
     KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
                 rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
                 nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr}
-#define SNR_RT_LATE(G, VPT)                                                 \
-    KernelEntry{OP_TAIL, ST_F32, 4, KIND_ROWTILE, G, VPT, rowtile_block<G>(), \
-                &launch_rowtile<OP_TAIL, ST_F32, G, VPT, true>, nullptr,    \
-                &occupancy_rowtile<OP_TAIL, ST_F32, G, VPT, true>, nullptr}
-#define SNR_SPLIT(OP, ST, VPT)                                              \
-    KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, VPT, SB, nullptr,      \
-                &launch_split<OP, ST, VPT>, &occupancy_split<OP, ST, VPT>,   \
+#define SNR_SPLIT(OP, ST)                                                   \
+    KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, 8, SB, nullptr,        \
+                &launch_split<OP, ST, 8>, &occupancy_split<OP, ST, 8>,      \
                 nullptr}
 #define SNR_MULTI(OP, ST)                                                   \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_MULTIPASS, MB, MVPT, MB, nullptr, \
                 nullptr, nullptr, &launch_multipass<OP, ST>}
 
-// The shapes compiled for one (operation, storage). Sub-wavefront groups
-// hold 4 vectors per lane; whole wavefronts and workgroups hold up to 16.
-#define SNR_SHAPES(OP, ST)                                                  \
+// The shapes the automatic choice can reach for one (operation, storage):
+// sub-wavefront groups with 4 vectors per lane, then one row per workgroup
+// with the smallest register tile that holds about two vectors per lane
+// (registers are allocated for every slot of a tile, used or not, and
+// occupancy follows them), then split and multi-pass.
+#define SNR_AUTO_SHAPES(OP, ST)                                             \
     SNR_RT(OP, ST, 1, 4), SNR_RT(OP, ST, 2, 4), SNR_RT(OP, ST, 4, 4),       \
     SNR_RT(OP, ST, 8, 4), SNR_RT(OP, ST, 16, 4), SNR_RT(OP, ST, 32, 4),     \
-    SNR_RT(OP, ST, 64, 2), SNR_RT(OP, ST, 64, 4), SNR_RT(OP, ST, 64, 8),    \
-    SNR_RT(OP, ST, 64, 16), SNR_RT(OP, ST, 128, 8), SNR_RT(OP, ST, 128, 13), \
-    SNR_RT(OP, ST, 128, 16), SNR_RT(OP, ST, 256, 4), SNR_RT(OP, ST, 256, 7), \
-    SNR_RT(OP, ST, 256, 8), SNR_RT(OP, ST, 256, 16), SNR_RT(OP, ST, 512, 4), \
-    SNR_RT(OP, ST, 512, 8), SNR_RT(OP, ST, 512, 16),                        \
+    SNR_RT(OP, ST, 128, 2), SNR_RT(OP, ST, 128, 8), SNR_RT(OP, ST, 256, 2), \
+    SNR_RT(OP, ST, 256, 4),                                                 \
+    SNR_RT(OP, ST, 512, 2), SNR_RT(OP, ST, 512, 4), SNR_RT(OP, ST, 1024, 1), \
     SNR_RT(OP, ST, 1024, 2), SNR_RT(OP, ST, 1024, 4),                       \
-    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST, 8), SNR_MULTI(OP, ST)
+    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST), SNR_MULTI(OP, ST)
 
-// 1024 lanes x 16 vectors only where the row fits in the 128 registers a
-// lane of a 1024-lane workgroup may use: not for 8-wide bf16, and for the
-// tail only with r loaded late (a/h resident, not a and r).
+// Further shapes, reachable only by forcing (shape sweeps and tests).
+#define SNR_SWEEP_SHAPES(OP, ST)                                            \
+    SNR_RT(OP, ST, 64, 2), SNR_RT(OP, ST, 64, 4), SNR_RT(OP, ST, 64, 8),    \
+    SNR_RT(OP, ST, 64, 16), SNR_RT(OP, ST, 128, 13), SNR_RT(OP, ST, 128, 16), \
+    SNR_RT(OP, ST, 256, 7), SNR_RT(OP, ST, 256, 8), SNR_RT(OP, ST, 256, 16), \
+    SNR_RT(OP, ST, 512, 8), SNR_RT(OP, ST, 512, 16)
+
+// 1024 lanes x 16 vectors only for 4-wide f32 rows: 8-wide 16-bit rows would
+// need 128 registers for the row alone (the tail and norm_then_add hold a/h
+// only, with r loaded late).
 const KernelEntry kTable[] = {
-    SNR_SHAPES(OP_PLAIN, ST_F32), SNR_RT(OP_PLAIN, ST_F32, 1024, 16),
-    SNR_SHAPES(OP_PLAIN, ST_BF16),
-    SNR_SHAPES(OP_TAIL, ST_F32),  SNR_RT_LATE(1024, 16),
+    SNR_AUTO_SHAPES(OP_PLAIN, ST_F32),    SNR_SWEEP_SHAPES(OP_PLAIN, ST_F32),
+    SNR_RT(OP_PLAIN, ST_F32, 1024, 16),
+    SNR_AUTO_SHAPES(OP_PLAIN, ST_BF16),   SNR_SWEEP_SHAPES(OP_PLAIN, ST_BF16),
+    SNR_AUTO_SHAPES(OP_PLAIN, ST_F16),
+    SNR_AUTO_SHAPES(OP_TAIL, ST_F32),     SNR_SWEEP_SHAPES(OP_TAIL, ST_F32),
+    SNR_RT(OP_TAIL, ST_F32, 1024, 16),
+    SNR_AUTO_SHAPES(OP_TAIL, ST_BF16),    SNR_AUTO_SHAPES(OP_TAIL, ST_F16),
+    SNR_AUTO_SHAPES(OP_NORM_ADD, ST_F32), SNR_RT(OP_NORM_ADD, ST_F32, 1024, 16),
+    SNR_AUTO_SHAPES(OP_NORM_ADD, ST_BF16), SNR_AUTO_SHAPES(OP_NORM_ADD, ST_F16),
+    SNR_AUTO_SHAPES(OP_ADD_NORM, ST_F32), SNR_RT(OP_ADD_NORM, ST_F32, 1024, 16),
+    SNR_AUTO_SHAPES(OP_ADD_NORM, ST_BF16), SNR_AUTO_SHAPES(OP_ADD_NORM, ST_F16),
 };
 
 }  // namespace

@@ -44,15 +44,48 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(F32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest even) as uint16 bits."""
+    return np.ascontiguousarray(x, dtype=F32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(F32)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in a storage type: float32 itself, or the 16-bit
+    patterns (uint16) of bf16 / f16."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=F32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
+    raise ValueError(dtype)
+
+
+def from_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float32 values of a storage array."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=F32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x)
+    if dtype == "f16":
+        return f16_bits_to_f32(x)
+    raise ValueError(dtype)
+
+
 # -- configurations ------------------------------------------------------------
 
 @dataclass(frozen=True)
 class Config:
     name: str
-    kind: str            # "plain" or "tail"
+    kind: str            # "plain", "tail", "norm_add" or "add_norm"
     rows: int
     n: int
-    dtype: str           # "f32" or "bf16" (storage type)
+    dtype: str           # "f32", "bf16" or "f16" (storage type)
     seed: int
     eps: tuple           # (eps,) for plain; (eps_post, eps_pre) for tail
     scale_exp: tuple = ()   # per-row log10 scale range(s)
@@ -82,6 +115,15 @@ def _configs() -> dict:
                (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
     add(Config("plain_16384x4096_bf16", "plain", 16384, 4096, "bf16", 401,
                (1e-6,), ((-2.0, 2.0),)))
+    # the tail in 16-bit storage, and its two halves on their own
+    add(Config("tail_4096x6656_bf16", "tail", 4096, 6656, "bf16", 302,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("tail_4096x6656_f16", "tail", 4096, 6656, "f16", 303,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("norm_add_4096x6656_f32", "norm_add", 4096, 6656, "f32", 311,
+               (EPS_POST,), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("add_norm_4096x6656_f32", "add_norm", 4096, 6656, "f32", 321,
+               (EPS_PRE,), ((-1.0, 1.0), (-3.0, 2.0))))
     for n in EDGE_NS:
         add(Config(f"edge_256x{n}_f32", "plain", 256, n, "f32", 500 + n,
                    (1e-5,), ((-12.0, 6.0),), edge=True))
@@ -143,11 +185,8 @@ def make_plain(cfg: Config, rows: int | None = None) -> dict:
         x = _edge_rows(rng, rows, cfg.n, lo, hi)
     else:
         x = _scaled_normal(rng, rows, cfg.n, lo, hi)
-    out = {"x": x, "gamma": gamma, "eps": cfg.eps[0]}
-    if cfg.dtype == "bf16":
-        out["x"] = f32_to_bf16_bits(x)
-        out["gamma"] = f32_to_bf16_bits(gamma)
-    return out
+    return {"x": to_storage(x, cfg.dtype), "gamma": to_storage(gamma, cfg.dtype),
+            "eps": cfg.eps[0], "dtype": cfg.dtype}
 
 
 def make_tail(cfg: Config, rows: int | None = None) -> dict:
@@ -161,13 +200,44 @@ def make_tail(cfg: Config, rows: int | None = None) -> dict:
     (alo, ahi), (rlo, rhi) = cfg.scale_exp
     a = _scaled_normal(rng, rows, cfg.n, alo, ahi)
     r = _scaled_normal(rng, rows, cfg.n, rlo, rhi)
-    return {"a": a, "r": r, "gamma_post": gamma_post, "gamma_pre": gamma_pre,
-            "eps_post": cfg.eps[0], "eps_pre": cfg.eps[1]}
+    st = cfg.dtype
+    return {"a": to_storage(a, st), "r": to_storage(r, st),
+            "gamma_post": to_storage(gamma_post, st),
+            "gamma_pre": to_storage(gamma_pre, st),
+            "eps_post": cfg.eps[0], "eps_pre": cfg.eps[1], "dtype": st}
+
+
+def make_pair(cfg: Config, rows: int | None = None) -> dict:
+    """Inputs for norm_add (a = block output, b = residual) and add_norm
+    (a = residual, b = block output): two rows streams, one gain, one eps."""
+    assert cfg.kind in ("norm_add", "add_norm")
+    rows = cfg.rows if rows is None else rows
+    rng = rng_for(cfg.seed)
+    gamma = _gamma(rng, cfg.n)
+    (alo, ahi), (blo, bhi) = cfg.scale_exp
+    a = _scaled_normal(rng, rows, cfg.n, alo, ahi)
+    b = _scaled_normal(rng, rows, cfg.n, blo, bhi)
+    st = cfg.dtype
+    return {"a": to_storage(a, st), "b": to_storage(b, st),
+            "gamma": to_storage(gamma, st), "eps": cfg.eps[0], "dtype": st}
 
 
 def make(cfg_or_name, rows: int | None = None) -> dict:
     cfg = CONFIGS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
-    return make_plain(cfg, rows) if cfg.kind == "plain" else make_tail(cfg, rows)
+    if cfg.kind == "plain":
+        return make_plain(cfg, rows)
+    if cfg.kind == "tail":
+        return make_tail(cfg, rows)
+    return make_pair(cfg, rows)
+
+
+def random_pair(kind: str, rows: int, n: int, seed: int,
+                dtype: str = "f32") -> dict:
+    """Ad-hoc inputs for norm_add / add_norm sweeps."""
+    cfg = Config(f"adhoc_{kind}_{rows}x{n}", kind, rows, n, dtype, seed,
+                 (EPS_POST if kind == "norm_add" else EPS_PRE,),
+                 ((-3.0, 2.0), (-1.0, 1.0)))
+    return make_pair(cfg)
 
 
 def random_plain(rows: int, n: int, seed: int, lo: float = -3.0,
@@ -178,8 +248,8 @@ def random_plain(rows: int, n: int, seed: int, lo: float = -3.0,
     return make_plain(cfg)
 
 
-def random_tail(rows: int, n: int, seed: int) -> dict:
+def random_tail(rows: int, n: int, seed: int, dtype: str = "f32") -> dict:
     """Ad-hoc tail inputs for shape sweeps (same recipe as the configs)."""
-    cfg = Config(f"adhoc_tail_{rows}x{n}", "tail", rows, n, "f32", seed,
+    cfg = Config(f"adhoc_tail_{rows}x{n}", "tail", rows, n, dtype, seed,
                  (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0)))
     return make_tail(cfg)

@@ -56,7 +56,7 @@ def test_error_codes_match_header():
     for name in ["SNR_OK", "SNR_ERR_NULL", "SNR_ERR_SHAPE", "SNR_ERR_DTYPE",
                  "SNR_ERR_EPS", "SNR_ERR_ALIAS", "SNR_ERR_ALIGN",
                  "SNR_ERR_WORKSPACE", "SNR_ERR_HIP", "SNR_ERR_DEVICE",
-                 "SNR_F32", "SNR_BF16"]:
+                 "SNR_F32", "SNR_BF16", "SNR_F16"]:
         assert header_enum(name) == getattr(_lib, name), name
     assert header_enum("SNR_SHAPE_ROWTILE") == _lib.SHAPE_ROWTILE
     assert header_enum("SNR_SHAPE_SPLIT") == _lib.SHAPE_SPLIT
@@ -96,7 +96,7 @@ def test_plain_argument_errors(L):
     assert plain(n=2 ** 31) == _lib.SNR_ERR_SHAPE
     assert plain(rows=-1) == _lib.SNR_ERR_SHAPE
     assert plain(rows=2 ** 62, n=2 ** 20) == _lib.SNR_ERR_SHAPE
-    assert plain(dtype=2) == _lib.SNR_ERR_DTYPE
+    assert plain(dtype=3) == _lib.SNR_ERR_DTYPE
     assert plain(dtype=-1) == _lib.SNR_ERR_DTYPE
     for bad in (0.0, -1e-5, math.nan, math.inf, -math.inf):
         assert plain(eps=bad) == _lib.SNR_ERR_EPS, bad
@@ -136,3 +136,70 @@ def test_force_shape_rejects_unknown_kind(L):
     buf = ctypes.create_string_buffer(8)
     assert L.snr_last_shape(None, 8) == _lib.SNR_ERR_NULL
     assert L.snr_last_shape(buf, 8) == _lib.SNR_OK
+
+
+R = BASE + (1 << 26)
+GQ = GAM + (1 << 20)
+
+
+def test_typed_and_inplace_tail_argument_errors(L):
+    f = _lib.sandwich_tail_typed
+    ok = dict(a=BASE, r=R, gp=GAM, ep=1e-8, gq=GQ, eq=1e-5, h=OUT,
+              y=OUT + (1 << 26), rows=4, n=64, dt=_lib.SNR_BF16)
+
+    def call(**kw):
+        k = {**ok, **kw}
+        return f(k["a"], k["r"], k["gp"], k["ep"], k["gq"], k["eq"], k["h"],
+                 k["y"], k["rows"], k["n"], k["dt"], 0)
+
+    assert call(dt=9) == _lib.SNR_ERR_DTYPE
+    assert call(a=BASE + 1) == _lib.SNR_ERR_ALIGN      # bf16 needs 2 bytes
+    assert call(dt=_lib.SNR_F32, a=BASE + 2) == _lib.SNR_ERR_ALIGN
+    assert call(y=R) == _lib.SNR_ERR_ALIAS
+    assert call(h=R + 2) == _lib.SNR_ERR_ALIAS
+    assert call(gp=0) == _lib.SNR_ERR_NULL
+    assert call(ep=-1.0) == _lib.SNR_ERR_EPS
+    assert call(rows=0, a=0, r=0, gp=0, gq=0, h=0, y=0) == _lib.SNR_OK
+    g = _lib.sandwich_tail_inplace
+    assert g(BASE, R, GAM, 1e-8, GQ, 1e-5, R, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # y over the residual
+    assert g(BASE, BASE, GAM, 1e-8, GQ, 1e-5, OUT, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # residual over a
+    assert g(BASE, R, GAM, 1e-8, GQ, 1e-5, OUT, 4, 64, 5, 0) == \
+        _lib.SNR_ERR_DTYPE
+
+
+def test_norm_then_add_argument_errors(L):
+    f = _lib.norm_then_add
+    SC = GAM + (1 << 22)
+    assert f(0, R, GAM, 1e-8, None, OUT, 4, 64, 0, 0) == _lib.SNR_ERR_NULL
+    assert f(BASE, R, GAM, 0.0, None, OUT, 4, 64, 0, 0) == _lib.SNR_ERR_EPS
+    assert f(BASE, R, GAM, 1e-8, SC + 1, OUT, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIGN                              # scale not f32-aligned
+    assert f(BASE, R, GAM, 1e-8, None, BASE, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # out over a
+    assert f(BASE, R, GAM, 1e-8, None, R + 4, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # out partly over r
+    assert f(BASE, R, GAM, 1e-8, R + 8, R, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # scale inside out
+    assert f(BASE, R, GAM, 1e-8, None, OUT, 4, 64, 3, 0) == \
+        _lib.SNR_ERR_DTYPE
+    assert f(0, 0, 0, 1e-8, None, 0, 0, 64, 0, 0) == _lib.SNR_OK
+
+
+def test_add_then_norm_argument_errors(L):
+    f = _lib.add_then_norm
+    Y = OUT + (1 << 26)
+    assert f(BASE, R, GAM, 1e-5, OUT, 0, 4, 64, 0, 0) == _lib.SNR_ERR_NULL
+    assert f(BASE, R, GAM, math.inf, OUT, Y, 4, 64, 0, 0) == _lib.SNR_ERR_EPS
+    assert f(BASE, R, GAM, 1e-5, OUT, BASE, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # y over a
+    assert f(BASE, R, GAM, 1e-5, OUT, OUT + 8, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # y over the sum
+    assert f(BASE, R, GAM, 1e-5, BASE + 4, Y, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # sum partly over a
+    assert f(BASE, R, GAM, 1e-5, GAM, Y, 4, 64, 0, 0) == \
+        _lib.SNR_ERR_ALIAS                              # sum over gamma
+    assert f(BASE, R, GAM, 1e-5, OUT, Y, 4, 64, _lib.SNR_F16 + 1, 0) == \
+        _lib.SNR_ERR_DTYPE
+    assert f(0, 0, 0, 1e-5, 0, 0, 0, 64, 0, 0) == _lib.SNR_OK

@@ -1,0 +1,165 @@
+"""GPU parity of the tail in 16-bit storage, the in-place tail, and the tail's
+two halves (norm_then_add, add_then_norm) against the f64 oracle.
+
+Every (operation, storage) pair runs every compiled dispatch shape (forced)
+on a ragged row, the full-size workloads run with the automatic choice, and
+the in-place and scaled forms are checked.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import sandwich_norm_residual_amd as snr  # noqa: E402
+from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
+from gpu_helpers import (check_add_norm, check_norm_add,  # noqa: E402
+                         check_plain, check_tail, run_add_norm, run_norm_add,
+                         run_plain, run_tail, say)
+
+pytestmark = pytest.mark.gpu
+
+VEC = {"f32": 4, "bf16": 8, "f16": 8}
+# row-tile shapes the automatic choice can reach (compiled for every pair)
+AUTO_ROWTILE = [(1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (32, 4), (128, 2),
+                (128, 8), (256, 2), (256, 4), (512, 2), (512, 4), (1024, 1),
+                (1024, 2), (1024, 4), (1024, 8)]
+PAIRS = [("tail", "bf16"), ("tail", "f16"), ("plain", "f16"),
+         ("norm_add", "f32"), ("norm_add", "bf16"), ("norm_add", "f16"),
+         ("add_norm", "f32"), ("add_norm", "bf16"), ("add_norm", "f16")]
+WIDE16 = {("norm_add", "f32"), ("add_norm", "f32")}
+
+
+def make_inputs(op, st, rows, n, seed):
+    if op == "plain":
+        return gen.random_plain(rows, n, seed, dtype=st)
+    if op == "tail":
+        return gen.random_tail(rows, n, seed, dtype=st)
+    return gen.random_pair(op, rows, n, seed, dtype=st)
+
+
+def run_and_check(oracle, op, inp, label, scale=None):
+    if op == "plain":
+        got, _ = run_plain(inp)
+        check_plain(oracle, inp, got, label)
+    elif op == "tail":
+        h, y = run_tail(inp)
+        check_tail(oracle, inp, h, y, label)
+    elif op == "norm_add":
+        out = run_norm_add(inp, scale=scale)
+        check_norm_add(oracle, inp, out, scale, label)
+    else:
+        s, y = run_add_norm(inp)
+        check_add_norm(oracle, inp, s, y, label)
+    return snr.last_shape()
+
+
+def _forced_cases():
+    cases = []
+    for op, st in PAIRS:
+        shapes = [("rowtile", g, v) for g, v in AUTO_ROWTILE]
+        if (op, st) in WIDE16:
+            shapes.append(("rowtile", 1024, 16))
+        shapes += [("split", 0, 8), ("multipass", 0, 8)]
+        for kind, g, v in shapes:
+            cases.append((op, st, kind, g, v))
+    return cases
+
+
+@pytest.mark.parametrize("case", _forced_cases(),
+                         ids=lambda c: "{}-{}-{}-g{}-v{}".format(*c))
+def test_forced_shape(oracle, case):
+    """Every compiled shape of the pair, on rows ragged by the largest
+    remainder (W - 1 elements past the last whole vector)."""
+    op, st, kind, g, v = case
+    w = VEC[st]
+    if kind == "rowtile":
+        nv = max(1, g * v - g // 2 - (1 if g == 1 else 0))
+    else:
+        nv = 2 * 2048 + 5          # three chunks of 256 x 8 vectors
+    n = nv * w + w - 1
+    rows = 19
+    label = f"{op}-{st}-{kind}-g{g}-v{v}-n{n}"
+    say(f"forced {label} rows={rows}")
+    inp = make_inputs(op, st, rows, n, 20000 + g * 7 + v + n)
+    with snr.forced_shape(kind, g, v):
+        shape = run_and_check(oracle, op, inp, label,
+                              scale=1.5 if op == "norm_add" else None)
+    if kind == "rowtile":
+        assert shape == f"rowtile:{g}:{v}:{w}", shape
+    else:
+        assert shape.startswith(f"{kind}:256:8:{w}:3"), shape
+
+
+@pytest.mark.parametrize("name", ["tail_4096x6656_bf16", "tail_4096x6656_f16",
+                                  "norm_add_4096x6656_f32",
+                                  "add_norm_4096x6656_f32"])
+def test_workload_full_size(oracle, name):
+    cfg = gen.CONFIGS[name]
+    say(f"workload {name}")
+    inp = gen.make(cfg)
+    run_and_check(oracle, cfg.kind, inp, name)
+
+
+@pytest.mark.parametrize("op_st", PAIRS + [("tail", "f32")])
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 9, 100, 6657, 65536 + 5])
+def test_ragged_auto(oracle, op_st, n):
+    op, st = op_st
+    rows = 13
+    say(f"ragged {op} {st} n={n}")
+    inp = make_inputs(op, st, rows, n, 21000 + n)
+    run_and_check(oracle, op, inp, f"ragged-{op}-{st}-{n}")
+
+
+@pytest.mark.parametrize("st", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [3, 6656, 65536])
+def test_tail_inplace(oracle, st, n):
+    """sandwich_tail_inplace updates the residual and returns y."""
+    rows = 11
+    say(f"tail in place {st} n={n}")
+    inp = gen.random_tail(rows, n, 22000 + n, dtype=st)
+    h, y = run_tail(inp, in_place=True)
+    check_tail(oracle, inp, h, y, f"tail-inplace-{st}-{n}")
+
+
+@pytest.mark.parametrize("st", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("scale", [None, 2.5, -0.75])
+def test_norm_add_scale_and_in_place(oracle, st, scale):
+    rows, n = 33, 4099
+    say(f"norm_add {st} scale={scale}")
+    inp = gen.random_pair("norm_add", rows, n, 23000, dtype=st)
+    out = run_norm_add(inp, scale=scale)
+    check_norm_add(oracle, inp, out, scale, f"norm-add-{st}-{scale}")
+    out_ip = run_norm_add(inp, scale=scale, in_place=True)
+    check_norm_add(oracle, inp, out_ip, scale, f"norm-add-inplace-{st}")
+    assert np.array_equal(out, out_ip)
+
+
+@pytest.mark.parametrize("st", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("into", ["a", "b"])
+def test_add_norm_in_place(oracle, st, into):
+    rows, n = 21, 2051
+    say(f"add_norm in place {st} into {into}")
+    inp = gen.random_pair("add_norm", rows, n, 24000, dtype=st)
+    s, y = run_add_norm(inp, sum_into=into)
+    check_add_norm(oracle, inp, s, y, f"add-norm-into-{into}-{st}")
+    s2, y2 = run_add_norm(inp)
+    assert np.array_equal(s, s2) and np.array_equal(y, y2)
+
+
+def test_stored_intermediate_is_what_the_second_norm_reads():
+    """With bf16 storage, the tail's y is the norm of h as stored, and
+    add_then_norm's y the norm of the stored sum: the fused call agrees with
+    the unfused plain norm of the stored intermediate to f32 rounding."""
+    from gpu_helpers import dev, host_f64
+    rows, n = 64, 6656
+    inp = gen.random_tail(rows, n, 25000, dtype="bf16")
+    a, r = dev(inp["a"], "bf16"), dev(inp["r"], "bf16")
+    gp, gq = dev(inp["gamma_post"], "bf16"), dev(inp["gamma_pre"], "bf16")
+    h, y = snr.sandwich_tail(a, r, gp, 1e-8, gq, 1e-5)
+    y2 = snr.rmsnorm_fwd(h, gq, 1e-5)
+    torch.cuda.synchronize()
+    d = np.abs(host_f64(y) - host_f64(y2))
+    # identical inputs to the second norm: at most one bf16 unit apart
+    # (the two reductions add in different orders)
+    assert np.all(d <= 2.0 ** -7 * np.abs(host_f64(y2)) + 1e-30)
+    assert np.mean(d == 0) > 0.99

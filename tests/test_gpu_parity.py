@@ -15,84 +15,27 @@ torch = pytest.importorskip("torch")
 import sandwich_norm_residual_amd as snr  # noqa: E402
 from sandwich_norm_residual_amd import _lib  # noqa: E402
 from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
-from parity import (TOL_BF16, TOL_F32, bf16_as_f64, plain_error,  # noqa: E402
-                    tail_errors)
+from gpu_helpers import (DEV, check_plain, check_tail, dev,  # noqa: E402
+                         host_f64, run_plain, run_tail, say)
 
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
 
 # Row-tile shapes compiled for every (operation, storage); 1024 x 16 exists
 # only where the row fits the registers of a 1024-lane workgroup.
 ROWTILE_SHAPES = [(1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (32, 4),
-                  (64, 2), (64, 4), (64, 8), (64, 16), (128, 8), (128, 13),
-                  (128, 16), (256, 4), (256, 7), (256, 8), (256, 16),
-                  (512, 4), (512, 8), (512, 16), (1024, 2), (1024, 4),
-                  (1024, 8)]
+                  (64, 2), (64, 4), (64, 8), (64, 16), (128, 2), (128, 8),
+                  (128, 13), (128, 16), (256, 2), (256, 4), (256, 7),
+                  (256, 8), (256, 16), (512, 2), (512, 4), (512, 8),
+                  (512, 16), (1024, 1), (1024, 2), (1024, 4), (1024, 8)]
 WIDE_EXTRA = {("plain", "f32"), ("tail", "f32")}
-VEC = {"f32": 4, "bf16": 8}   # elements per 128-bit vector
-
-
-def say(msg):
-    print(f"[gpu-case] {msg}", flush=True)
-
-
-def dev_f32(a):
-    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
-
-
-def dev_bf16(bits):
-    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
-    return t.to(DEV).view(torch.bfloat16)
-
-
-def host_f64(t):
-    if t.dtype == torch.bfloat16:
-        return bf16_as_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
-    return t.cpu().numpy().astype(np.float64)
-
-
-def run_plain(inp, prefill=float("nan"), out_is_x=False):
-    bf16 = inp["x"].dtype == np.uint16
-    x = dev_bf16(inp["x"]) if bf16 else dev_f32(inp["x"])
-    g = dev_bf16(inp["gamma"]) if bf16 else dev_f32(inp["gamma"])
-    out = x if out_is_x else torch.full_like(x, prefill)
-    snr.rmsnorm_fwd(x, g, inp["eps"], out=out)
-    torch.cuda.synchronize()
-    return host_f64(out), out
-
-
-def run_tail(inp, prefill=float("nan"), in_place=False):
-    a, r = dev_f32(inp["a"]), dev_f32(inp["r"])
-    gp, gq = dev_f32(inp["gamma_post"]), dev_f32(inp["gamma_pre"])
-    h = r if in_place else torch.full_like(a, prefill)
-    y = torch.full_like(a, prefill)
-    snr.sandwich_tail(a, r, gp, inp["eps_post"], gq, inp["eps_pre"],
-                      h_out=h, y_out=y)
-    torch.cuda.synchronize()
-    return host_f64(h), host_f64(y)
-
-
-def check_plain(oracle, inp, got, label):
-    want = oracle.rmsnorm(inp["x"], inp["gamma"], inp["eps"])
-    tol = TOL_BF16 if inp["x"].dtype == np.uint16 else TOL_F32
-    err = plain_error(got, want)
-    say(f"{label}: max rel err {err:.3e} (tol {tol:g}) shape {snr.last_shape()}")
-    assert err <= tol, (label, err)
-    return err
-
-
-def check_tail(oracle, inp, h, y, label):
-    o = oracle.sandwich_tail(inp["a"], inp["r"], inp["gamma_post"],
-                             inp["eps_post"], inp["gamma_pre"], inp["eps_pre"])
-    eh, ey = tail_errors(h, y, o, inp["r"], inp["gamma_pre"])
-    say(f"{label}: h err {eh:.3e} y err {ey:.3e} shape {snr.last_shape()}")
-    assert eh <= TOL_F32 and ey <= TOL_F32, (label, eh, ey)
+VEC = {"f32": 4, "bf16": 8, "f16": 8}   # elements per 128-bit vector
 
 
 # ---------------------------------------------------------------------------
 # Every configuration, full size, automatic shape (what the benchmark runs)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", list(gen.CONFIGS))
+@pytest.mark.parametrize("name", [k for k, c in gen.CONFIGS.items()
+                                  if c.kind in ("plain", "tail")])
 def test_config_full_size(oracle, name):
     cfg = gen.CONFIGS[name]
     say(f"config {name} rows={cfg.rows} n={cfg.n} {cfg.dtype}")
@@ -290,10 +233,10 @@ def test_misaligned_base_pointer(oracle, n):
     inp = gen.random_plain(rows, n, 6000 + n)
     buf = torch.empty(rows * n + 1, device=DEV)
     x = buf[1:].view(rows, n)
-    x.copy_(dev_f32(inp["x"]))
+    x.copy_(dev(inp["x"], "f32"))
     gbuf = torch.empty(n + 1, device=DEV)
     g = gbuf[1:]
-    g.copy_(dev_f32(inp["gamma"]))
+    g.copy_(dev(inp["gamma"], "f32"))
     ybuf = torch.full((rows * n + 1,), float("nan"), device=DEV)
     y = ybuf[1:].view(rows, n)
     snr.rmsnorm_fwd(x, g, inp["eps"], out=y)
@@ -368,8 +311,8 @@ def test_non_default_stream(oracle):
     inp = gen.make("tail_8x6656_f32")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        a, r = dev_f32(inp["a"]), dev_f32(inp["r"])
-        gp, gq = dev_f32(inp["gamma_post"]), dev_f32(inp["gamma_pre"])
+        a, r = dev(inp["a"], "f32"), dev(inp["r"], "f32")
+        gp, gq = dev(inp["gamma_post"], "f32"), dev(inp["gamma_pre"], "f32")
         h, y = snr.sandwich_tail(a, r, gp, inp["eps_post"], gq,
                                  inp["eps_pre"])
     s.synchronize()
@@ -383,7 +326,7 @@ def test_bf16_output_is_round_to_nearest_even(oracle):
     unit away."""
     say("bf16 rounding")
     inp = gen.make("plain_16384x4096_bf16", rows=512)
-    x, g = dev_bf16(inp["x"]), dev_bf16(inp["gamma"])
+    x, g = dev(inp["x"], "bf16"), dev(inp["gamma"], "bf16")
     y = snr.rmsnorm_fwd(x, g, inp["eps"])
     torch.cuda.synchronize()
     bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
