@@ -40,12 +40,14 @@ def log(msg: str) -> None:
 
 # row streams (reads + writes) and gains of each operation
 STREAMS = {"plain": (2, 1), "tail": (4, 2), "norm_add": (3, 1),
-           "add_norm": (4, 1)}
+           "add_norm": (4, 1), "multi": (2, 1)}
 
 
 def algorithmic_bytes(cfg) -> int:
     es = 4 if cfg.dtype == "f32" else 2
     streams, gains = STREAMS[cfg.kind]
+    if cfg.kind == "multi":
+        gains = len(cfg.segments)
     return streams * cfg.rows * cfg.n * es + gains * cfg.n * es
 
 
@@ -92,6 +94,12 @@ def to_device(arr, dtype, torch):
 def make_device_sets(cfg, inp, sets, torch):
     """`sets` copies of the row inputs and their own outputs; gains shared."""
     st = cfg.dtype
+    if cfg.kind == "multi":
+        xs = [to_device(x, st, torch) for x in inp["xs"]]
+        gs = [to_device(g, st, torch) for g in inp["gammas"]]
+        return [{"xs": [x.clone() for x in xs], "gs": gs,
+                 "out": [torch.empty_like(x) for x in xs]}
+                for _ in range(sets)]
     rows_keys = {"plain": ("x",), "tail": ("a", "r"),
                  "norm_add": ("a", "b"), "add_norm": ("a", "b")}[cfg.kind]
     gain_keys = ("gamma_post", "gamma_pre") if cfg.kind == "tail" else \
@@ -107,7 +115,7 @@ def make_device_sets(cfg, inp, sets, torch):
     return out
 
 
-def make_step(cfg, inp, sets, snr):
+def make_step(cfg, inp, sets, snr, separate=False):
     kind = cfg.kind
 
     def step(i):
@@ -121,6 +129,13 @@ def make_step(cfg, inp, sets, snr):
         elif kind == "norm_add":
             snr.norm_then_add(s["a"], s["b"], s["gamma"], inp["eps"],
                               out=s["out"][0])
+        elif kind == "multi" and separate:
+            for x, g, y in zip(s["xs"], s["gs"], s["out"]):
+                snr.rmsnorm_fwd(x, g, inp["eps"], out=y)
+        elif kind == "multi":
+            snr.rmsnorm_fwd_multi(
+                [(x, g, inp["eps"]) for x, g in zip(s["xs"], s["gs"])],
+                s["out"])
         else:
             snr.add_then_norm(s["a"], s["b"], s["gamma"], inp["eps"],
                               sum_out=s["out"][0], y_out=s["out"][1])
@@ -147,9 +162,21 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
     f = {k: from_storage(v, st) for k, v in inp.items()
          if isinstance(v, np.ndarray)}
 
+    if cfg.kind == "multi":
+        f = {"xs": [from_storage(x, st) for x in inp["xs"]],
+             "gammas": [from_storage(g, st) for g in inp["gammas"]]}
+
     def one(b):
         lo, hi = b
-        if cfg.kind == "tail":
+        if cfg.kind == "multi":
+            # rows of the concatenated segments [lo, hi)
+            start = 0
+            for x, g in zip(f["xs"], f["gammas"]):
+                a, z = max(lo - start, 0), min(hi - start, x.shape[0])
+                if a < z:
+                    O.rmsnorm(x[a:z], g, inp["eps"])
+                start += x.shape[0]
+        elif cfg.kind == "tail":
             O.sandwich_tail(f["a"][lo:hi], f["r"][lo:hi], f["gamma_post"],
                             inp["eps_post"], f["gamma_pre"], inp["eps_pre"])
         elif cfg.kind == "plain":
@@ -200,6 +227,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle CPU baseline")
+    ap.add_argument("--separate-launches", action="store_true",
+                    help="several-norm workloads: one rmsnorm_fwd launch per "
+                         "problem instead of one rmsnorm_fwd_multi launch")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run 10 plain device copies of MIB MiB "
                          "(byte-counter calibration under rocprofv3)")
@@ -229,7 +259,7 @@ def main() -> int:
     stream = torch.cuda.Stream()   # default priority
     nbytes = algorithmic_bytes(cfg)
 
-    step = make_step(cfg, inp, sets, snr)
+    step = make_step(cfg, inp, sets, snr, args.separate_launches)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -308,6 +338,8 @@ def main() -> int:
                  "with log-uniform per-row scales, gains 1+0.1*N(0,1)"),
         "config": {"workload": cfg.name, "rows": cfg.rows, "n": cfg.n,
                    "kind": cfg.kind, "eps": list(cfg.eps),
+                   "launches_per_step": (len(cfg.segments)
+                                         if args.separate_launches else 1),
                    "dispatch_shape": shape,
                    "rotating_buffer_sets": len(sets),
                    "algorithmic_bytes_per_step": nbytes},

@@ -185,6 +185,33 @@ SNR_API int add_then_norm(const void *a, const void *b, const void *gamma,
                           float eps, void *sum_out, void *y_out, int64_t rows,
                           int64_t n, int dtype, hipStream_t stream);
 
+/*
+ * rmsnorm_fwd_multi - several independent RMSNorms of one row width in one
+ * launch, e.g. the per-head query and key norms of a layer. The Muser book's
+ * per-token accounting ("RMSNorm and the dual-epsilon sandwich", section
+ * 12.5) counts these per-head norms at head_dim 128 as the second-largest
+ * family of norm dispatches (two per layer); one launch here replaces two.
+ * Each segment is an ordinary rmsnorm_fwd problem:
+ *     y[i, j] = x[i, j] / sqrt(mean_k x[i, k]^2 + eps) * gamma[j]
+ *   segments  host array of `count` (1..SNR_MAX_SEGMENTS) descriptors, read
+ *             during the call only
+ *   n, dtype  shared row width and storage type
+ * Within a segment y == x is allowed; a segment's y may not overlap any
+ * other segment's x or y, nor any gain. Segments with rows == 0 are skipped.
+ * Rows too wide for one register tile (over 65536 f32 elements) fall back to
+ * one rmsnorm_fwd launch per segment.
+ */
+#define SNR_MAX_SEGMENTS 8
+typedef struct {
+    const void *x;     /* [rows, n] input */
+    const void *gamma; /* [n] gain */
+    void *y;           /* [rows, n] output */
+    int64_t rows;
+    float eps;
+} snr_segment;
+SNR_API int rmsnorm_fwd_multi(const snr_segment *segments, int count,
+                              int64_t n, int dtype, hipStream_t stream);
+
 /* Human-readable text for an SNR_* code (static storage, never NULL). */
 SNR_API const char *snr_strerror(int code);
 

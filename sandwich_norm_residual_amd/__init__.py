@@ -11,6 +11,7 @@ the current stream) into those calls. Nothing here computes.
                                  gamma_pre, eps_pre)   # residual updated
     out  = norm_then_add(a, r, gamma, eps, out_scale=None)
     s, y = add_then_norm(a, b, gamma, eps)
+    yq, yk = rmsnorm_fwd_multi([(q, gamma_q, eps), (k, gamma_k, eps)])
 
 Definitions: "RMSNorm and the dual-epsilon sandwich" (Muser book chapter
 12), section 12.1 for RMSNorm and sections 12.2 and 12.4.3 for the tail;
@@ -24,14 +25,23 @@ import contextlib
 from . import _lib
 from ._lib import SnrError
 
-__all__ = ["rmsnorm_fwd", "sandwich_tail", "sandwich_tail_inplace",
-           "norm_then_add", "add_then_norm", "forced_shape", "last_shape",
-           "split_timeouts", "SnrError"]
+__all__ = ["rmsnorm_fwd", "rmsnorm_fwd_multi", "sandwich_tail",
+           "sandwich_tail_inplace", "norm_then_add", "add_then_norm",
+           "forced_shape", "last_shape", "split_timeouts", "SnrError"]
 
 
 def _torch():
     import torch
     return torch
+
+
+def _on(dev):
+    """A context that makes `dev` current only when it is not already (the
+    switch costs a few microseconds per call)."""
+    torch = _torch()
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
 
 
 def _dtype_code(t) -> int:
@@ -84,12 +94,46 @@ def rmsnorm_fwd(x, gamma, eps: float, out=None):
         out = torch.empty_like(x)
     else:
         _check_tensor("out", out, x.device, x.dtype, x.shape)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         rc = _lib.rmsnorm_fwd(x.data_ptr(), gamma.data_ptr(), float(eps),
                               rows, n, _dtype_code(x), out.data_ptr(), stream)
     _lib.check(rc, "rmsnorm_fwd")
     return out
+
+
+def rmsnorm_fwd_multi(problems, outs=None):
+    """Several RMSNorms of one row width and dtype in one launch.
+
+    problems: sequence of (x, gamma, eps) with x [..., n] and gamma [n], all
+    on one device; outs: optional matching outputs (``out is x`` computes in
+    place). Returns the list of outputs. Up to 8 problems per call."""
+    torch = _torch()
+    if not problems:
+        return []
+    if len(problems) > _lib.MAX_SEGMENTS:
+        raise ValueError(f"at most {_lib.MAX_SEGMENTS} problems per call")
+    x0 = problems[0][0]
+    _dtype_code(x0)
+    n = x0.shape[-1]
+    outs = list(outs) if outs is not None else [None] * len(problems)
+    segs = []
+    for i, (x, g, eps) in enumerate(problems):
+        _check_tensor(f"x[{i}]", x, x0.device, x0.dtype)
+        rows, nn = _rows_n(x)
+        if nn != n:
+            raise ValueError("all problems must share the row width")
+        _check_tensor(f"gamma[{i}]", g, x0.device, x0.dtype, (n,))
+        if outs[i] is None:
+            outs[i] = torch.empty_like(x)
+        _check_tensor(f"out[{i}]", outs[i], x0.device, x0.dtype, x.shape)
+        segs.append((x.data_ptr(), g.data_ptr(), outs[i].data_ptr(), rows,
+                     float(eps)))
+    with _on(x0.device):
+        rc = _lib.rmsnorm_fwd_multi(segs, n, _dtype_code(x0),
+                                    _stream(x0.device))
+    _lib.check(rc, "rmsnorm_fwd_multi")
+    return outs
 
 
 def _stream(dev):
@@ -126,7 +170,7 @@ def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
     h_out = torch.empty_like(a) if h_out is None else h_out
     y_out = torch.empty_like(a) if y_out is None else y_out
     _rows_inputs([("h_out", h_out), ("y_out", y_out)], [], a)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         if a.dtype == torch.float32:
             rc = _lib.sandwich_tail(a.data_ptr(), r.data_ptr(),
                                     gamma_post.data_ptr(), float(eps_post),
@@ -154,7 +198,7 @@ def sandwich_tail_inplace(a, residual, gamma_post, eps_post: float,
                             ("gamma_pre", gamma_pre)], a)
     y_out = torch.empty_like(a) if y_out is None else y_out
     _rows_inputs([("y_out", y_out)], [], a)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = _lib.sandwich_tail_inplace(
             a.data_ptr(), residual.data_ptr(), gamma_post.data_ptr(),
             float(eps_post), gamma_pre.data_ptr(), float(eps_pre),
@@ -178,7 +222,7 @@ def norm_then_add(a, r, gamma, eps: float, out_scale=None, out=None):
         if out_scale.numel() < 1:
             raise ValueError("out_scale must hold one element")
         scale_ptr = out_scale.data_ptr()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = _lib.norm_then_add(a.data_ptr(), r.data_ptr(), gamma.data_ptr(),
                                 float(eps), scale_ptr, out.data_ptr(), rows,
                                 n, _dtype_code(a), _stream(a.device))
@@ -194,7 +238,7 @@ def add_then_norm(a, b, gamma, eps: float, sum_out=None, y_out=None):
     sum_out = torch.empty_like(a) if sum_out is None else sum_out
     y_out = torch.empty_like(a) if y_out is None else y_out
     _rows_inputs([("sum_out", sum_out), ("y_out", y_out)], [], a)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = _lib.add_then_norm(a.data_ptr(), b.data_ptr(), gamma.data_ptr(),
                                 float(eps), sum_out.data_ptr(),
                                 y_out.data_ptr(), rows, n, _dtype_code(a),

@@ -32,6 +32,15 @@ SHAPE_ROWTILE = 1
 SHAPE_SPLIT = 2
 SHAPE_MULTIPASS = 3
 
+MAX_SEGMENTS = 8
+
+
+class Segment(ctypes.Structure):
+    """snr_segment: one RMSNorm problem of a rmsnorm_fwd_multi call."""
+    _fields_ = [("x", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("eps", ctypes.c_float)]
+
 # Every function include/snr.h declares, with its ctypes signature.
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -49,6 +58,8 @@ SIGNATURES = {
                              _vp]),
     "add_then_norm": (_int, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _int,
                              _vp]),
+    "rmsnorm_fwd_multi": (_int, [ctypes.POINTER(Segment), _int, _i64, _int,
+                                 _vp]),
     "snr_strerror": (ctypes.c_char_p, [_int]),
     "snr_last_hip_error": (_int, []),
     "snr_force_shape": (_int, [_int, _int, _int]),
@@ -132,6 +143,14 @@ def add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n, dtype,
                   stream) -> int:
     return lib().add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n,
                                dtype, stream)
+
+
+def rmsnorm_fwd_multi(segments, n, dtype, stream) -> int:
+    """segments: sequence of (x, gamma, y, rows, eps) with integer device
+    addresses."""
+    arr = (Segment * max(len(segments), 1))(
+        *[Segment(x, g, y, rows, eps) for x, g, y, rows, eps in segments])
+    return lib().rmsnorm_fwd_multi(arr, len(segments), n, dtype, stream)
 
 
 def force_shape(kind: int, g: int = 0, vpt: int = 0) -> None:

@@ -390,6 +390,9 @@ int tail_impl(const void *a, const void *r, const void *gamma_post,
 
 using namespace snr;
 
+static_assert(SNR_MAX_SEGMENTS == kMaxSegments,
+              "segment table size differs between the ABI and the kernels");
+
 extern "C" {
 
 int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t rows,
@@ -493,6 +496,85 @@ int add_then_norm(const void *a, const void *b, const void *gamma, float eps,
     args.rows = rows;
     args.n = (int32_t)n;
     return launch(OP_ADD_NORM, st, es, args, stream);
+}
+
+int rmsnorm_fwd_multi(const snr_segment *segs, int count, int64_t n,
+                      int dtype, hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    if (!segs) return SNR_ERR_NULL;
+    if (count < 1 || count > kMaxSegments) return SNR_ERR_SHAPE;
+    int64_t total = 0;
+    for (int s = 0; s < count; ++s) {
+        const snr_segment &g = segs[s];
+        int rc = check_common(g.rows, n, es, {g.eps}, {g.x, g.gamma, g.y});
+        if (rc > 0) return rc;
+        if (g.rows > INT64_MAX - total) return SNR_ERR_SHAPE;
+        total += g.rows;
+    }
+    if (total == 0) return SNR_OK;
+    const int64_t gb = n * es;
+    for (int s = 0; s < count; ++s) {
+        const snr_segment &a = segs[s];
+        if (a.rows == 0) continue;
+        const int64_t ta = a.rows * n * es;
+        if (a.y != a.x && overlaps(a.y, ta, a.x, ta)) return SNR_ERR_ALIAS;
+        for (int t = 0; t < count; ++t) {
+            const snr_segment &b = segs[t];
+            if (b.rows == 0) continue;
+            const int64_t tb = b.rows * n * es;
+            if (overlaps(a.y, ta, b.gamma, gb)) return SNR_ERR_ALIAS;
+            if (t != s && (overlaps(a.y, ta, b.x, tb) ||
+                           overlaps(a.y, ta, b.y, tb)))
+                return SNR_ERR_ALIAS;
+        }
+    }
+
+    int dev = 0;
+    DeviceInfo info;
+    int rc = current_device(&dev, &info);
+    if (rc != SNR_OK) return rc;
+    const int w = (int)(16 / es);
+    Choice c;
+    rc = choose(OP_PLAIN, st, w, n / w, &c);
+    if (rc != SNR_OK) return rc;
+    if (c.k->kind != KIND_ROWTILE || !c.k->multi) {
+        // rows too wide for one register tile (or a forced shape without a
+        // several-segment kernel): one ordinary launch per segment
+        for (int s = 0; s < count; ++s) {
+            if (segs[s].rows == 0) continue;
+            rc = rmsnorm_fwd(segs[s].x, segs[s].gamma, segs[s].eps,
+                             segs[s].rows, n, dtype, segs[s].y, stream);
+            if (rc != SNR_OK) return rc;
+        }
+        return SNR_OK;
+    }
+    MultiArgs m{};
+    m.count = count;
+    m.n = (int32_t)n;
+    m.nv = (int32_t)(n / w);
+    m.rem = (int32_t)(n % w);
+    m.row_start[0] = 0;
+    for (int s = 0; s < count; ++s) {
+        m.x[s] = segs[s].x;
+        m.g[s] = segs[s].gamma;
+        m.y[s] = segs[s].y;
+        m.eps[s] = segs[s].eps;
+        m.row_start[s + 1] = m.row_start[s] + segs[s].rows;
+    }
+    const KernelEntry *k = c.k;
+    const int rpb = k->block / k->g;
+    const int64_t step = (int64_t)(UINT32_MAX / (uint32_t)k->block) * rpb;
+    for (int64_t r0 = 0; r0 < total; r0 += step) {
+        const int64_t nr = total - r0 < step ? total - r0 : step;
+        hipError_t e = k->multi(m, r0, nr, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    std::snprintf(t_last_shape, sizeof t_last_shape, "multi:%d:%d:%d:%d",
+                  k->g, k->vpt, w, count);
+    t_last_hip_error = 0;
+    return SNR_OK;
 }
 
 const char *snr_strerror(int code) {

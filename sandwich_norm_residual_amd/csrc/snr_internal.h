@@ -34,6 +34,22 @@ struct RowArgs {
     int32_t rem;   // elements after the last whole vector (n % W)
 };
 
+// Several independent RMSNorms in one launch: segment s covers global rows
+// [row_start[s], row_start[s + 1]) with its own tensors and epsilon; all
+// segments share the row width and storage type.
+constexpr int kMaxSegments = 8;
+struct MultiArgs {
+    const void *x[kMaxSegments];
+    const void *g[kMaxSegments];
+    void *y[kMaxSegments];
+    float eps[kMaxSegments];
+    int64_t row_start[kMaxSegments + 1];
+    int32_t count;
+    int32_t n;
+    int32_t nv;
+    int32_t rem;
+};
+
 // Cross-workgroup state of the split-row kernels (device memory, owned by a
 // per-(device, stream) workspace). Every field starts at zero and every
 // launch leaves it at zero again (see the split kernel).
@@ -57,6 +73,8 @@ using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
                                    int64_t row0, int64_t nrows, int chunks,
                                    int groups, hipStream_t);
 using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
+using MultiLaunch = hipError_t (*)(const MultiArgs &, int64_t row0,
+                                   int64_t nrows, hipStream_t);
 using MultipassLaunch = hipError_t (*)(const RowArgs &, float *scratch,
                                        int64_t row0, int64_t nrows,
                                        int chunks, hipStream_t);
@@ -77,6 +95,7 @@ struct KernelEntry {
     SplitLaunch split;
     OccupancyQuery occupancy;
     MultipassLaunch multipass;
+    MultiLaunch multi;   // several segments in one launch (row tile only)
 };
 
 // The table of compiled kernels (defined in snr_kernels.hip).

@@ -478,6 +478,36 @@ rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
         [&](float s, int which) { return row_total<G>(s, red[which]); });
 }
 
+// Several RMSNorms in one launch (the same row tile as above): each row
+// finds its segment in the table and normalises with that segment's
+// tensors and epsilon.
+template <int ST, int G, int VPT>
+__global__ void __launch_bounds__(rowtile_block<G>())
+multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
+    constexpr int BLOCK = rowtile_block<G>();
+    constexpr int RPB = BLOCK / G;
+    constexpr int WPR = G > 64 ? G / 64 : 1;
+    __shared__ float red[2][WPR];
+
+    const int sub = threadIdx.x & (G - 1);
+    const int64_t row = row0 + (int64_t)blockIdx.x * RPB + threadIdx.x / G;
+    const bool live = row < row_end;
+    int seg = 0;
+    while (seg + 1 < m.count && row >= m.row_start[seg + 1]) ++seg;
+    RowArgs p{};
+    p.x0 = m.x[seg];
+    p.g0 = m.g[seg];
+    p.out0 = m.y[seg];
+    p.eps0 = m.eps[seg];
+    p.n = m.n;
+    p.nv = m.nv;
+    p.rem = m.rem;
+    const int64_t off = live ? (row - m.row_start[seg]) * (int64_t)m.n : 0;
+    process_row<OP_PLAIN, ST, VPT, rowtile_extra<ST, G>(), false>(
+        p, off, live, sub, G, sub, G, true,
+        [&](float s, int which) { return row_total<G>(s, red[which]); });
+}
+
 // ---------------------------------------------------------------------------
 // Split-row kernel: chunk c of rows g, g + groups, ... for workgroup
 // (g, c) of a cooperative grid of groups x chunks workgroups.
@@ -742,6 +772,23 @@ hipError_t occupancy_rowtile(int *blocks_per_cu) {
         blocks_per_cu, rowtile_kernel<OP, ST, G, VPT>, rowtile_block<G>(), 0);
 }
 
+template <int ST, int G, int VPT>
+hipError_t launch_multi(const MultiArgs &m, int64_t row0, int64_t nrows,
+                        hipStream_t stream) {
+    constexpr int BLOCK = rowtile_block<G>();
+    constexpr int RPB = BLOCK / G;
+    const int64_t blocks = (nrows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((multi_kernel<ST, G, VPT>), dim3((unsigned int)blocks),
+                       dim3(BLOCK), 0, stream, m, row0, row0 + nrows);
+    return hipGetLastError();
+}
+
+template <int OP, int ST, int G, int VPT>
+constexpr MultiLaunch multi_for() {
+    if constexpr (OP == OP_PLAIN) return &launch_multi<ST, G, VPT>;
+    else return nullptr;
+}
+
 template <int OP, int ST, int VPT>
 hipError_t launch_split(const RowArgs &p, const SplitState &st, int64_t row0,
                         int64_t nrows, int chunks, int groups,
@@ -802,17 +849,22 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
     return hipGetLastError();
 }
 
-#define SNR_RT(OP, ST, G, VPT)                                              \
+// Plain row tiles on the automatic menu also get the several-segment
+// launcher; the sweep-only shapes do not.
+#define SNR_RT_M(OP, ST, G, VPT, M)                                         \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
                 rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
-                nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr}
+                nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr, M}
+#define SNR_RT(OP, ST, G, VPT) SNR_RT_M(OP, ST, G, VPT, nullptr)
+#define SNR_RT_A(OP, ST, G, VPT)                                            \
+    SNR_RT_M(OP, ST, G, VPT, (multi_for<OP, ST, G, VPT>()))
 #define SNR_SPLIT(OP, ST)                                                   \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, 8, SB, nullptr,        \
                 &launch_split<OP, ST, 8>, &occupancy_split<OP, ST, 8>,      \
-                nullptr}
+                nullptr, nullptr}
 #define SNR_MULTI(OP, ST)                                                   \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_MULTIPASS, MB, MVPT, MB, nullptr, \
-                nullptr, nullptr, &launch_multipass<OP, ST>}
+                nullptr, nullptr, &launch_multipass<OP, ST>, nullptr}
 
 // The shapes the automatic choice can reach for one (operation, storage):
 // sub-wavefront groups with 4 vectors per lane, then one row per workgroup
@@ -820,13 +872,14 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 // (registers are allocated for every slot of a tile, used or not, and
 // occupancy follows them), then split and multi-pass.
 #define SNR_AUTO_SHAPES(OP, ST)                                             \
-    SNR_RT(OP, ST, 1, 4), SNR_RT(OP, ST, 2, 4), SNR_RT(OP, ST, 4, 4),       \
-    SNR_RT(OP, ST, 8, 4), SNR_RT(OP, ST, 16, 4), SNR_RT(OP, ST, 32, 4),     \
-    SNR_RT(OP, ST, 128, 2), SNR_RT(OP, ST, 128, 8), SNR_RT(OP, ST, 256, 2), \
-    SNR_RT(OP, ST, 256, 4),                                                 \
-    SNR_RT(OP, ST, 512, 2), SNR_RT(OP, ST, 512, 4), SNR_RT(OP, ST, 1024, 1), \
-    SNR_RT(OP, ST, 1024, 2), SNR_RT(OP, ST, 1024, 4),                       \
-    SNR_RT(OP, ST, 1024, 8), SNR_SPLIT(OP, ST), SNR_MULTI(OP, ST)
+    SNR_RT_A(OP, ST, 1, 4), SNR_RT_A(OP, ST, 2, 4), SNR_RT_A(OP, ST, 4, 4), \
+    SNR_RT_A(OP, ST, 8, 4), SNR_RT_A(OP, ST, 16, 4),                        \
+    SNR_RT_A(OP, ST, 32, 4), SNR_RT_A(OP, ST, 128, 2),                      \
+    SNR_RT_A(OP, ST, 128, 8), SNR_RT_A(OP, ST, 256, 2),                     \
+    SNR_RT_A(OP, ST, 256, 4), SNR_RT_A(OP, ST, 512, 2),                     \
+    SNR_RT_A(OP, ST, 512, 4), SNR_RT_A(OP, ST, 1024, 1),                    \
+    SNR_RT_A(OP, ST, 1024, 2), SNR_RT_A(OP, ST, 1024, 4),                   \
+    SNR_RT_A(OP, ST, 1024, 8), SNR_SPLIT(OP, ST), SNR_MULTI(OP, ST)
 
 // Further shapes, reachable only by forcing (shape sweeps and tests).
 #define SNR_SWEEP_SHAPES(OP, ST)                                            \
@@ -840,7 +893,7 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 // only, with r loaded late).
 const KernelEntry kTable[] = {
     SNR_AUTO_SHAPES(OP_PLAIN, ST_F32),    SNR_SWEEP_SHAPES(OP_PLAIN, ST_F32),
-    SNR_RT(OP_PLAIN, ST_F32, 1024, 16),
+    SNR_RT_A(OP_PLAIN, ST_F32, 1024, 16),
     SNR_AUTO_SHAPES(OP_PLAIN, ST_BF16),   SNR_SWEEP_SHAPES(OP_PLAIN, ST_BF16),
     SNR_AUTO_SHAPES(OP_PLAIN, ST_F16),
     SNR_AUTO_SHAPES(OP_TAIL, ST_F32),     SNR_SWEEP_SHAPES(OP_TAIL, ST_F32),

@@ -82,7 +82,7 @@ def from_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 @dataclass(frozen=True)
 class Config:
     name: str
-    kind: str            # "plain", "tail", "norm_add" or "add_norm"
+    kind: str            # "plain", "tail", "norm_add", "add_norm", "multi"
     rows: int
     n: int
     dtype: str           # "f32", "bf16" or "f16" (storage type)
@@ -90,6 +90,7 @@ class Config:
     eps: tuple           # (eps,) for plain; (eps_post, eps_pre) for tail
     scale_exp: tuple = ()   # per-row log10 scale range(s)
     edge: bool = False   # structured rows 0-5 + log-uniform mean-square
+    segments: tuple = ()  # rows of each problem of a several-norm workload
     notes: str = field(default="", compare=False)
 
 
@@ -124,6 +125,12 @@ def _configs() -> dict:
                (EPS_POST,), ((-3.0, 2.0), (-1.0, 1.0))))
     add(Config("add_norm_4096x6656_f32", "add_norm", 4096, 6656, "f32", 321,
                (EPS_PRE,), ((-1.0, 1.0), (-3.0, 2.0))))
+    # per-head query and key norms of one layer (head_dim 128; 52 query and
+    # 8 key heads per token): one token, and a 512-token prefill
+    add(Config("qknorm_decode_f32", "multi", 60, 128, "f32", 331, (1e-5,),
+               ((-2.0, 1.0),), segments=(52, 8)))
+    add(Config("qknorm_prefill_bf16", "multi", 512 * 60, 128, "bf16", 332,
+               (1e-5,), ((-2.0, 2.0),), segments=(512 * 52, 512 * 8)))
     for n in EDGE_NS:
         add(Config(f"edge_256x{n}_f32", "plain", 256, n, "f32", 500 + n,
                    (1e-5,), ((-12.0, 6.0),), edge=True))
@@ -222,12 +229,28 @@ def make_pair(cfg: Config, rows: int | None = None) -> dict:
             "gamma": to_storage(gamma, st), "eps": cfg.eps[0], "dtype": st}
 
 
+def make_multi(cfg: Config) -> dict:
+    """Inputs for a several-norm workload: one (x, gamma) per segment, all of
+    width n, drawn in segment order."""
+    assert cfg.kind == "multi"
+    rng = rng_for(cfg.seed)
+    lo, hi = cfg.scale_exp[0]
+    xs, gs = [], []
+    for rows in cfg.segments:
+        gs.append(to_storage(_gamma(rng, cfg.n), cfg.dtype))
+        xs.append(to_storage(_scaled_normal(rng, rows, cfg.n, lo, hi),
+                             cfg.dtype))
+    return {"xs": xs, "gammas": gs, "eps": cfg.eps[0], "dtype": cfg.dtype}
+
+
 def make(cfg_or_name, rows: int | None = None) -> dict:
     cfg = CONFIGS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
     if cfg.kind == "plain":
         return make_plain(cfg, rows)
     if cfg.kind == "tail":
         return make_tail(cfg, rows)
+    if cfg.kind == "multi":
+        return make_multi(cfg)
     return make_pair(cfg, rows)
 
 

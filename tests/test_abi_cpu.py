@@ -203,3 +203,31 @@ def test_add_then_norm_argument_errors(L):
     assert f(BASE, R, GAM, 1e-5, OUT, Y, 4, 64, _lib.SNR_F16 + 1, 0) == \
         _lib.SNR_ERR_DTYPE
     assert f(0, 0, 0, 1e-5, 0, 0, 0, 64, 0, 0) == _lib.SNR_OK
+
+
+def test_multi_argument_errors(L):
+    Seg = _lib.Segment
+
+    def call(segs, count=None, n=64, dt=0):
+        arr = (Seg * max(len(segs), 1))(*segs)
+        return L.rmsnorm_fwd_multi(arr, len(segs) if count is None else count,
+                                   n, dt, 0)
+
+    good = Seg(BASE, GAM, OUT, 4, 1e-5)
+    other = Seg(R, GQ, OUT + (1 << 26), 8, 1e-5)
+    assert call([good], count=0) == _lib.SNR_ERR_SHAPE
+    assert call([good] * 9) == _lib.SNR_ERR_SHAPE
+    assert L.rmsnorm_fwd_multi(None, 1, 64, 0, 0) == _lib.SNR_ERR_NULL
+    assert call([good, Seg(0, GQ, OUT + (1 << 26), 8, 1e-5)]) == \
+        _lib.SNR_ERR_NULL
+    assert call([good, Seg(R, GQ, OUT + (1 << 26), 8, 0.0)]) == \
+        _lib.SNR_ERR_EPS
+    assert call([good, other], dt=7) == _lib.SNR_ERR_DTYPE
+    assert call([good, Seg(R, GQ, OUT + 4, 8, 1e-5)]) == \
+        _lib.SNR_ERR_ALIAS                          # outputs overlap
+    assert call([good, Seg(OUT, GQ, OUT + (1 << 26), 8, 1e-5)]) == \
+        _lib.SNR_ERR_ALIAS                          # y of one is x of another
+    assert call([good, Seg(R, OUT, OUT + (1 << 26), 8, 1e-5)]) == \
+        _lib.SNR_ERR_ALIAS                          # a gain inside an output
+    assert call([Seg(0, 0, 0, 0, 1e-5), Seg(0, 0, 0, 0, 1e-5)]) == \
+        _lib.SNR_OK                                 # nothing to do
