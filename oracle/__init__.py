@@ -23,6 +23,9 @@ Definitions followed (cited by page title and section):
   rmsNormThenAddThenBroadcastScaleKernel: (rmsnorm(a) + r) * scale.
 * ``add_then_norm``: same page, residualAddRmsNormKernel: s = a + b and
   rmsnorm(s), both returned, s kept in f64.
+* ``rmsnorm_q8_1``: same page, "Fused RMSNorm + Q8_1 quantize": per block of
+  32 normalised values, d = amax / 127 and q = round-half-even(x / d)
+  clamped to int8 (a zero block gives d = 0, q = 0).
 """
 from __future__ import annotations
 
@@ -87,9 +90,11 @@ class Oracle:
                                                  vp, vp, vp]
         lib.snr_oracle_add_then_norm.argtypes = [vp, vp, vp, ctypes.c_float,
                                                  _i64, _i64, vp, vp, vp, vp]
+        lib.snr_oracle_rmsnorm_q8_1.argtypes = [vp, vp, ctypes.c_float, _i64,
+                                                _i64, vp, vp, vp, vp, vp]
         for f in (lib.snr_oracle_rmsnorm_f32, lib.snr_oracle_rmsnorm_bf16,
                   lib.snr_oracle_sandwich_tail, lib.snr_oracle_norm_then_add,
-                  lib.snr_oracle_add_then_norm):
+                  lib.snr_oracle_add_then_norm, lib.snr_oracle_rmsnorm_q8_1):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -188,6 +193,30 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected arguments (code {rc})")
         return s, y, d
+
+
+    # -- RMSNorm followed by Q8_1 quantisation ---------------------------
+    def rmsnorm_q8_1(self, x: np.ndarray, gamma: np.ndarray, eps: float):
+        """float32 x [rows, n] (n a multiple of 32), gamma [n]. Returns
+        (y, d, t, q): normalised rows (f64), block scales d = amax/127 (f64,
+        [rows, n/32]), t = y/d (f64; 0 in zero blocks) and the int8 codes
+        round-half-even(t) clamped to [-128, 127]."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+        if x.ndim != 2 or gamma.shape != (x.shape[1],):
+            raise ValueError("x must be [rows, n] and gamma [n]")
+        rows, n = x.shape
+        y = np.empty((rows, n), np.float64)
+        d = np.empty((rows, max(n // 32, 0)), np.float64)
+        t = np.empty((rows, n), np.float64)
+        q = np.empty((rows, n), np.int8)
+        work = np.empty(2 * max(n, 1), np.float64)
+        rc = self._lib.snr_oracle_rmsnorm_q8_1(
+            _ptr(x), _ptr(gamma), float(eps), rows, n, _ptr(y), _ptr(d),
+            _ptr(t), _ptr(q), _ptr(work))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (code {rc})")
+        return y, d, t, q
 
 
 _DEFAULT: Oracle | None = None

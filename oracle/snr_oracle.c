@@ -228,3 +228,63 @@ int snr_oracle_add_then_norm(const float *a, const float *b,
     }
     return ORACLE_OK;
 }
+
+/*
+ * RMSNorm followed by Q8_1 quantisation of the normalised row, the fused
+ * epilogue on Hesper's "RMSNorm Layer" page ("Fused RMSNorm + Q8_1
+ * quantize", fusedRMSNormQ8_1Kernel). Phase 1 is the RMSNorm of section
+ * 12.1 of the Muser chapter (x / rms * gamma). Phase 2 takes each block of
+ * 32 consecutive normalised values and
+ *   amax = max |x_normed|          over the block
+ *   d    = amax / 127
+ *   q    = round(x_normed / d)     to nearest, ties to even (WGSL round),
+ *                                  clamped to [-128, 127]
+ * A block whose amax is 0 has d = 0 and q = 0 (the division is undefined;
+ * reading: a zero block encodes as zeros).
+ * Everything in double; n must be a multiple of 32.
+ * Outputs: y (rows*n normalised values), d (rows*n/32 block scales),
+ * t (rows*n values x_normed / d, 0 where d = 0), q (rows*n codes).
+ * work: 2*n doubles.
+ */
+int snr_oracle_rmsnorm_q8_1(const float *x, const float *gamma, float eps,
+                            int64_t rows, int64_t n, double *y, double *d,
+                            double *t, int8_t *q, double *work)
+{
+    if (n < 32 || n % 32 != 0 || rows < 0 || !x || !gamma || !y || !d ||
+        !t || !q || !work)
+        return ORACLE_EBADARG;
+    double *xr = work, *gr = work + n;
+    for (int64_t j = 0; j < n; ++j)
+        gr[j] = (double)gamma[j];
+    const int64_t nb = n / 32;
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            xr[j] = (double)x[i * n + j];
+        double *yi = y + i * n;
+        rms_row(xr, gr, (double)eps, n, yi);
+        for (int64_t b = 0; b < nb; ++b) {
+            double amax = 0.0;
+            for (int64_t l = 0; l < 32; ++l)
+                if (fabs(yi[b * 32 + l]) > amax)
+                    amax = fabs(yi[b * 32 + l]);
+            const double db = amax / 127.0;
+            d[i * nb + b] = db;
+            for (int64_t l = 0; l < 32; ++l) {
+                const int64_t j = i * n + b * 32 + l;
+                if (db == 0.0) {
+                    t[j] = 0.0;
+                    q[j] = 0;
+                    continue;
+                }
+                t[j] = yi[b * 32 + l] / db;
+                double r = nearbyint(t[j]);   /* ties to even (default mode) */
+                if (r > 127.0)
+                    r = 127.0;
+                if (r < -128.0)
+                    r = -128.0;
+                q[j] = (int8_t)r;
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -500,6 +500,88 @@ def pin_decimal_halves(O):
         assert abs(d[0] - float(dd)) <= 1e-14 * float(dd)
 
 
+# ---------------------------------------------------------------------------
+# RMSNorm + Q8_1 (Hesper "RMSNorm Layer", Fused RMSNorm + Q8_1 quantize)
+# ---------------------------------------------------------------------------
+
+def _near_tie(t, band=1e-9):
+    f = np.abs(np.asarray(t) - np.floor(t) - 0.5)
+    return f < band
+
+
+def pin_q8_closed_form(O):
+    """gamma = 1, block x = 1..32: q_j = round(127 j / 32) (ties to even;
+    the tie at j = 16 is not decided here, see _near_tie), and
+    d = 32 / sqrt(357.5 + eps) / 127 since mean(j^2) = 33 * 65 / 6."""
+    x = np.arange(1, 33, dtype=F32)[None, :]
+    y, d, t, q = O.rmsnorm_q8_1(x, np.ones(32, F32), 1e-5)
+    want_t = 127.0 * np.arange(1, 33) / 32.0
+    ok = ~_near_tie(want_t)
+    assert np.all(q[0][ok] == np.array([round(v) for v in want_t])[ok])
+    assert np.max(np.abs(t[0] - want_t)) < 1e-12
+    wd = 32.0 / math.sqrt(357.5 + _f(1e-5)) / 127.0
+    assert abs(d[0, 0] - wd) < 1e-15
+    # negated row: negated codes
+    _, _, _, qn = O.rmsnorm_q8_1(-x, np.ones(32, F32), 1e-5)
+    assert np.array_equal(qn[0][ok], -q[0][ok])
+
+
+def pin_q8_properties(O):
+    """Every nonzero block reaches |q| = 127 at its largest value; d * q is
+    within d / 2 of the normalised value; a zero block encodes as d = 0,
+    q = 0; codes do not depend on the row's scale (inv_rms cancels in
+    x_normed / d)."""
+    rng = rng_for(41)
+    for n in (32, 64, 320):
+        x = (rng.standard_normal((6, n)) * 10.0 ** rng.uniform(-3, 3, (6, 1))
+             ).astype(F32)
+        x[2, 32:64] = 0.0 if n >= 64 else x[2, 32:64]
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        y, d, t, q = O.rmsnorm_q8_1(x, g, 1e-5)
+        nb = n // 32
+        qb = q.reshape(6, nb, 32).astype(np.int32)
+        yb = y.reshape(6, nb, 32)
+        for i in range(6):
+            for b in range(nb):
+                if np.all(yb[i, b] == 0):
+                    assert d[i, b] == 0 and np.all(qb[i, b] == 0)
+                    continue
+                assert np.max(np.abs(qb[i, b])) == 127
+                assert np.all(np.abs(d[i, b] * qb[i, b] - yb[i, b]) <=
+                              d[i, b] * (0.5 + 1e-9))
+        y2, d2, t2, q2 = O.rmsnorm_q8_1((x * F32(8.0)).astype(F32), g, 1e-5)
+        ok = ~_near_tie(t) & ~_near_tie(t2)
+        assert np.array_equal(q[ok], q2[ok])
+
+
+def pin_q8_decimal(O):
+    """Exact decimal arithmetic on short rows: codes agree away from ties,
+    scales to 1e-14."""
+    from decimal import ROUND_HALF_EVEN
+    getcontext().prec = 50
+    rng = rng_for(42)
+    for it in range(12):
+        n = 32 * int(rng.integers(1, 4))
+        x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-2, 2)).astype(F32)
+        g = (1 + 0.1 * rng.standard_normal(n)).astype(F32)
+        yd, _ = _dec_rms([Decimal(float(v)) for v in x],
+                         [Decimal(float(v)) for v in g], Decimal(_f(1e-5)))
+        y, d, t, q = O.rmsnorm_q8_1(x[None, :], g, 1e-5)
+        for b in range(n // 32):
+            blk = yd[b * 32:(b + 1) * 32]
+            amax = max(abs(v) for v in blk)
+            db = amax / Decimal(127)
+            assert abs(d[0, b] - float(db)) <= 1e-14 * float(db)
+            for l, v in enumerate(blk):
+                tv = v / db
+                frac = abs(tv - tv.to_integral_value(rounding="ROUND_FLOOR")
+                           - Decimal("0.5"))
+                if frac < Decimal("1e-9"):
+                    continue
+                qv = int(tv.to_integral_value(rounding=ROUND_HALF_EVEN))
+                assert q[0, b * 32 + l] == max(-128, min(127, qv)), (it, b, l)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_constant_rows,
@@ -521,4 +603,7 @@ ALL_PINS = [
     pin_halves_compose_to_the_tail,
     pin_halves_torch,
     pin_decimal_halves,
+    pin_q8_closed_form,
+    pin_q8_properties,
+    pin_q8_decimal,
 ]
