@@ -45,6 +45,9 @@ STREAMS = {"plain": (2, 1), "tail": (4, 2), "norm_add": (3, 1),
 
 def algorithmic_bytes(cfg) -> int:
     es = 4 if cfg.dtype == "f32" else 2
+    if cfg.kind == "q8":
+        # read x and gamma; write one 36-byte record per 32 elements
+        return cfg.rows * cfg.n * es + cfg.n * es + cfg.rows * cfg.n // 32 * 36
     streams, gains = STREAMS[cfg.kind]
     if cfg.kind == "multi":
         gains = len(cfg.segments)
@@ -100,6 +103,14 @@ def make_device_sets(cfg, inp, sets, torch):
         return [{"xs": [x.clone() for x in xs], "gs": gs,
                  "out": [torch.empty_like(x) for x in xs]}
                 for _ in range(sets)]
+    if cfg.kind == "q8":
+        x = to_device(inp["x"], st, torch)
+        g = to_device(inp["gamma"], st, torch)
+        blocks = (cfg.rows, cfg.n // 32, 36)
+        return [{"x": x.clone(), "gamma": g,
+                 "out": [torch.empty(blocks, dtype=torch.uint8,
+                                     device=x.device)]}
+                for _ in range(sets)]
     rows_keys = {"plain": ("x",), "tail": ("a", "r"),
                  "norm_add": ("a", "b"), "add_norm": ("a", "b")}[cfg.kind]
     gain_keys = ("gamma_post", "gamma_pre") if cfg.kind == "tail" else \
@@ -126,6 +137,8 @@ def make_step(cfg, inp, sets, snr, separate=False):
                               h_out=s["out"][0], y_out=s["out"][1])
         elif kind == "plain":
             snr.rmsnorm_fwd(s["x"], s["gamma"], inp["eps"], out=s["out"][0])
+        elif kind == "q8":
+            snr.rmsnorm_q8_1(s["x"], s["gamma"], inp["eps"], out=s["out"][0])
         elif kind == "norm_add":
             snr.norm_then_add(s["a"], s["b"], s["gamma"], inp["eps"],
                               out=s["out"][0])
@@ -181,6 +194,8 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
                             inp["eps_post"], f["gamma_pre"], inp["eps_pre"])
         elif cfg.kind == "plain":
             O.rmsnorm(f["x"][lo:hi], f["gamma"], inp["eps"])
+        elif cfg.kind == "q8":
+            O.rmsnorm_q8_1(f["x"][lo:hi], f["gamma"], inp["eps"])
         elif cfg.kind == "norm_add":
             O.norm_then_add(f["a"][lo:hi], f["b"][lo:hi], f["gamma"],
                             inp["eps"])

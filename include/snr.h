@@ -186,6 +186,30 @@ SNR_API int add_then_norm(const void *a, const void *b, const void *gamma,
                           int64_t n, int dtype, hipStream_t stream);
 
 /*
+ * rmsnorm_q8_1 - RMSNorm whose output goes straight into Q8_1 records, for a
+ * following 8-bit matmul. Hesper's "RMSNorm Layer" page, "Fused RMSNorm +
+ * Q8_1 quantize" (fusedRMSNormQ8_1Kernel): each row is normalised as in
+ * rmsnorm_fwd, then every block of 32 consecutive normalised values v[0..31]
+ * is encoded as
+ *     d    = max_k |v[k]| / 127              (f32, stored as f16)
+ *     q[k] = round(v[k] / d), ties to even, clamped to [-128, 127]
+ * and a block whose values are all zero encodes as d = 0, q = 0.
+ *   x      [rows, n] of `dtype`; n must be a multiple of 32 (else
+ *          SNR_ERR_SHAPE);  gamma [n] of `dtype`
+ *   out    rows * (n / 32) records of 36 bytes, row-major, block b of row i
+ *          at byte (i * n / 32 + b) * 36:
+ *            bytes 0-1  d as IEEE binary16 (round to nearest even)
+ *            bytes 2-3  s, always 0 (a consumer that reads s gets 0)
+ *            bytes 4-35 q[0..31] as int8
+ *          4-byte aligned (else SNR_ERR_ALIGN); may overlap neither x nor
+ *          gamma (SNR_ERR_ALIAS).
+ * The codes are computed with the f32 scale d, before its rounding to f16.
+ */
+SNR_API int rmsnorm_q8_1(const void *x, const void *gamma, float eps,
+                         int64_t rows, int64_t n, int dtype, void *out,
+                         hipStream_t stream);
+
+/*
  * rmsnorm_fwd_multi - several independent RMSNorms of one row width in one
  * launch, e.g. the per-head query and key norms of a layer. The Muser book's
  * per-token accounting ("RMSNorm and the dual-epsilon sandwich", section

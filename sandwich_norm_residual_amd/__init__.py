@@ -12,11 +12,13 @@ the current stream) into those calls. Nothing here computes.
     out  = norm_then_add(a, r, gamma, eps, out_scale=None)
     s, y = add_then_norm(a, b, gamma, eps)
     yq, yk = rmsnorm_fwd_multi([(q, gamma_q, eps), (k, gamma_k, eps)])
+    blocks = rmsnorm_q8_1(x, gamma, eps)   # uint8 [..., n / 32, 36]
 
 Definitions: "RMSNorm and the dual-epsilon sandwich" (Muser book chapter
 12), section 12.1 for RMSNorm and sections 12.2 and 12.4.3 for the tail;
 Hesper's "RMSNorm Layer" page for norm_then_add (rmsNormThenAdd kernels)
-and add_then_norm (residualAddRmsNormKernel).
+and add_then_norm (residualAddRmsNormKernel), and its "Fused RMSNorm + Q8_1
+quantize" section for rmsnorm_q8_1.
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ from ._lib import SnrError
 
 __all__ = ["rmsnorm_fwd", "rmsnorm_fwd_multi", "sandwich_tail",
            "sandwich_tail_inplace", "norm_then_add", "add_then_norm",
+           "rmsnorm_q8_1", "q8_1_fields",
            "forced_shape", "last_shape", "split_timeouts", "SnrError"]
 
 
@@ -245,6 +248,45 @@ def add_then_norm(a, b, gamma, eps: float, sum_out=None, y_out=None):
                                 _stream(a.device))
     _lib.check(rc, "add_then_norm")
     return sum_out, y_out
+
+
+def rmsnorm_q8_1(x, gamma, eps: float, out=None):
+    """RMSNorm of each row of x, encoded as Q8_1 records: per 32 values a
+    36-byte record {f16 d, f16 s = 0, int8 q[32]} with d = amax / 127 and
+    q = round-half-even(v / d) clamped to [-128, 127].
+
+    x: contiguous [..., n] GPU tensor (float32, bfloat16 or float16) with n a
+    multiple of 32; gamma: [n] of the same dtype. Returns (or fills ``out``)
+    a uint8 tensor [..., n / 32, 36]."""
+    torch = _torch()
+    _dtype_code(x)
+    _check_tensor("x", x, x.device, x.dtype)
+    rows, n = _rows_n(x)
+    _check_tensor("gamma", gamma, x.device, x.dtype, (n,))
+    if n % 32:
+        raise ValueError(f"rmsnorm_q8_1 needs n a multiple of 32, got {n}")
+    shape = tuple(x.shape[:-1]) + (n // 32, 36)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    else:
+        _check_tensor("out", out, x.device, torch.uint8, shape)
+    with _on(x.device):
+        rc = _lib.rmsnorm_q8_1(x.data_ptr(), gamma.data_ptr(), float(eps),
+                               rows, n, _dtype_code(x), out.data_ptr(),
+                               _stream(x.device))
+    _lib.check(rc, "rmsnorm_q8_1")
+    return out
+
+
+def q8_1_fields(blocks):
+    """Split Q8_1 records (uint8 [..., 36], any device) into their fields:
+    (d as float16 [...], s as float16 [...], q as int8 [..., 32]). A view
+    of the bytes only; nothing is computed."""
+    b = blocks.contiguous()
+    d = b[..., 0:2].contiguous().view(_torch().float16)[..., 0]
+    s = b[..., 2:4].contiguous().view(_torch().float16)[..., 0]
+    q = b[..., 4:36].contiguous().view(_torch().int8)
+    return d, s, q
 
 
 @contextlib.contextmanager

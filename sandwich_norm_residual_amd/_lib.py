@@ -58,6 +58,7 @@ SIGNATURES = {
                              _vp]),
     "add_then_norm": (_int, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _int,
                              _vp]),
+    "rmsnorm_q8_1": (_int, [_vp, _vp, _f, _i64, _i64, _int, _vp, _vp]),
     "rmsnorm_fwd_multi": (_int, [ctypes.POINTER(Segment), _int, _i64, _int,
                                  _vp]),
     "snr_strerror": (ctypes.c_char_p, [_int]),
@@ -143,6 +144,10 @@ def add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n, dtype,
                   stream) -> int:
     return lib().add_then_norm(a, b, gamma, eps, sum_out, y_out, rows, n,
                                dtype, stream)
+
+
+def rmsnorm_q8_1(x, gamma, eps, rows, n, dtype, out, stream) -> int:
+    return lib().rmsnorm_q8_1(x, gamma, eps, rows, n, dtype, out, stream)
 
 
 def rmsnorm_fwd_multi(segments, n, dtype, stream) -> int:

@@ -186,9 +186,11 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
         c->chunks = split_chunks(c->k, nv);
         return SNR_OK;
     }
+    // Q8_1 records need each 32-element block inside one lane group
+    const int gmin = op == OP_NORM_Q8 ? 32 / w : 1;
     if (nv <= 128) {
         // several rows per wavefront: 4 vectors per lane
-        int g = 1;
+        int g = gmin;
         while (g * 4 < nv) g *= 2;
         c->k = find_entry(op, st, w, KIND_ROWTILE, g, 4);
         return c->k ? SNR_OK : SNR_ERR_SHAPE;
@@ -209,8 +211,10 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
         if (!best || e.vpt < best->vpt) best = &e;
     }
     if (!best) {
-        // no register tile holds the row: split it across workgroups
+        // no register tile holds the row: split it across workgroups (or,
+        // for an operation without a split kernel, use the multi-pass one)
         c->k = find_entry(op, st, w, KIND_SPLIT, 0, 8);
+        if (!c->k) c->k = find_entry(op, st, w, KIND_MULTIPASS, 0, kMultiVpt);
         if (!c->k) return SNR_ERR_SHAPE;
         c->chunks = split_chunks(c->k, nv);
         return SNR_OK;
@@ -317,7 +321,11 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
                       k->vpt, w, c.chunks);
     if (debug_enabled())
         std::fprintf(stderr, "[snr] %s rows=%lld n=%d -> %s\n",
-                     op == OP_TAIL ? "sandwich_tail" : "rmsnorm_fwd",
+                     op == OP_TAIL       ? "sandwich_tail"
+                     : op == OP_NORM_ADD ? "norm_then_add"
+                     : op == OP_ADD_NORM ? "add_then_norm"
+                     : op == OP_NORM_Q8  ? "rmsnorm_q8_1"
+                                         : "rmsnorm_fwd",
                      (long long)a.rows, a.n, t_last_shape);
     t_last_hip_error = 0;
     return SNR_OK;
@@ -496,6 +504,29 @@ int add_then_norm(const void *a, const void *b, const void *gamma, float eps,
     args.rows = rows;
     args.n = (int32_t)n;
     return launch(OP_ADD_NORM, st, es, args, stream);
+}
+
+int rmsnorm_q8_1(const void *x, const void *gamma, float eps, int64_t rows,
+                 int64_t n, int dtype, void *out, hipStream_t stream) {
+    int64_t es = 0;
+    const int st = storage_of(dtype, &es);
+    if (st < 0) return SNR_ERR_DTYPE;
+    if (n % 32 != 0) return SNR_ERR_SHAPE;
+    int rc = check_common(rows, n, es, {eps}, {x, gamma, out});
+    if (rc != SNR_OK) return rc < 0 ? SNR_OK : rc;
+    if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return SNR_ERR_ALIGN;
+    const int64_t ob = rows * (n / 32) * 36, tb = rows * n * es, gb = n * es;
+    if (overlaps(out, ob, x, tb) || overlaps(out, ob, gamma, gb))
+        return SNR_ERR_ALIAS;
+
+    RowArgs a{};
+    a.x0 = x;
+    a.g0 = gamma;
+    a.out0 = out;
+    a.eps0 = eps;
+    a.rows = rows;
+    a.n = (int32_t)n;
+    return launch(OP_NORM_Q8, st, es, a, stream);
 }
 
 int rmsnorm_fwd_multi(const snr_segment *segs, int count, int64_t n,

@@ -7,7 +7,13 @@
 
 namespace snr {
 
-enum Op : int { OP_PLAIN = 0, OP_TAIL = 1, OP_NORM_ADD = 2, OP_ADD_NORM = 3 };
+enum Op : int {
+    OP_PLAIN = 0,
+    OP_TAIL = 1,
+    OP_NORM_ADD = 2,
+    OP_ADD_NORM = 3,
+    OP_NORM_Q8 = 4  // RMSNorm, then Q8_1 records of the normalised row
+};
 enum Storage : int { ST_F32 = 0, ST_BF16 = 1, ST_F16 = 2 };
 enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2, KIND_MULTIPASS = 3 };
 

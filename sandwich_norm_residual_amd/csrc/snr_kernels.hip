@@ -509,6 +509,106 @@ multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm followed by Q8_1 quantisation (Hesper "RMSNorm Layer", fused
+// RMSNorm + Q8_1): each block of 32 normalised values becomes a 36-byte
+// record {f16 d, f16 s = 0, int8 q[32]} with d = amax / 127 and
+// q = round-half-even(x / d) clamped to [-128, 127] (a zero block: d = 0,
+// q = 0). Codes are packed four per 32-bit word, element 4k in the low
+// byte. n is a multiple of 32, so a block is BV = 32 / W consecutive
+// vectors, held by BV consecutive lanes of one row group (G a multiple of
+// BV): the block's amax is a DPP max over those lanes.
+// ---------------------------------------------------------------------------
+template <int Q>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (Q >= 2) v = fmaxf(v, dpp<0xB1>(v));   // lane ^ 1
+    if constexpr (Q >= 4) v = fmaxf(v, dpp<0x4E>(v));   // lane ^ 2
+    if constexpr (Q >= 8) v = fmaxf(v, dpp<0x141>(v));  // 8-lane halves
+    return v;
+}
+
+__device__ __forceinline__ unsigned int q8_code(float y, float d) {
+    if (d == 0.0f) return 0u;
+    const float r = fminf(fmaxf(rintf(y / d), -128.0f), 127.0f);
+    return (unsigned int)(int)r & 0xFFu;
+}
+
+// Quantise one lane's vector of normalised values y[W] (vector index i of a
+// row whose Q8_1 records start at `rec`); every lane of the wavefront must
+// call it (the amax is a cross-lane max). `valid` masks the stores.
+template <int W>
+__device__ __forceinline__ void q8_vector(const float (&y)[W], int i,
+                                          bool valid, unsigned char *rec) {
+    constexpr int BV = 32 / W;
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < W; ++e) m = fmaxf(m, fabsf(y[e]));
+    const float amax = group_max<BV>(m);
+    const float d = amax / 127.0f;
+    if (!valid) return;
+    unsigned char *blk = rec + (int64_t)(i / BV) * 36;
+    unsigned int words[W / 4];
+#pragma unroll
+    for (int w = 0; w < W / 4; ++w)
+        words[w] = q8_code(y[4 * w], d) | (q8_code(y[4 * w + 1], d) << 8) |
+                   (q8_code(y[4 * w + 2], d) << 16) |
+                   (q8_code(y[4 * w + 3], d) << 24);
+    unsigned int *qw = reinterpret_cast<unsigned int *>(blk + 4) +
+                       (i % BV) * (W / 4);
+#pragma unroll
+    for (int w = 0; w < W / 4; ++w) __builtin_nontemporal_store(words[w], qw + w);
+    if (i % BV == 0) {
+        const unsigned int hdr =
+            (unsigned int)__builtin_bit_cast(unsigned short, (_Float16)d);
+        __builtin_nontemporal_store(hdr, reinterpret_cast<unsigned int *>(blk));
+    }
+}
+
+template <int ST, int G, int VPT>
+__global__ void __launch_bounds__(rowtile_block<G>())
+q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
+    using C = Codec<ST>;
+    using T = typename C::T;
+    constexpr int W = C::W;
+    constexpr int BLOCK = rowtile_block<G>();
+    constexpr int RPB = BLOCK / G;
+    constexpr int WPR = G > 64 ? G / 64 : 1;
+    static_assert(G % (32 / W) == 0, "a Q8_1 block must lie in one lane group");
+    __shared__ float red[2][WPR];
+
+    const int sub = threadIdx.x & (G - 1);
+    const int64_t row = row0 + (int64_t)blockIdx.x * RPB + threadIdx.x / G;
+    const bool live = row < row_end;
+    const int64_t off = live ? row * (int64_t)p.n : 0;
+    const int nv = p.nv;
+    const T *x = static_cast<const T *>(p.x0) + off;
+
+    float v[VPT][W];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int i = k * G + sub;
+        if (live && i < nv) C::load_nt(x, i, v[k]); else zero(v[k]);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) s += sumsq<W>(v[k]);
+    const float inv = inv_rms(row_total<G>(s, red[0]), p.n, p.eps0);
+
+    const T *g = static_cast<const T *>(p.g0);
+    unsigned char *rec = static_cast<unsigned char *>(p.out0) +
+                         (live ? row : 0) * (int64_t)(p.n / 32) * 36;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int i = k * G + sub;
+        const bool valid = live && i < nv;
+        float gv[W], y[W];
+        if (valid) C::load(g, i, gv); else zero(gv);
+#pragma unroll
+        for (int e = 0; e < W; ++e) y[e] = v[k][e] * inv * gv[e];
+        q8_vector<W>(y, i, valid, rec);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-row kernel: chunk c of rows g, g + groups, ... for workgroup
 // (g, c) of a cooperative grid of groups x chunks workgroups.
 // ---------------------------------------------------------------------------
@@ -744,6 +844,42 @@ pass_fuse(RowArgs p, int64_t row0, int chunks, const float *inv, float *part) {
     }
 }
 
+// Q8_1 records of the normalised rows (rows too wide for one register
+// tile): y = x * inv * gain, quantised per block. Consecutive lanes hold
+// consecutive vectors, so a block is BV consecutive lanes of one wavefront.
+template <int ST>
+__global__ void __launch_bounds__(MB)
+pass_q8(RowArgs p, int64_t row0, int chunks, const float *inv) {
+    using C = Codec<ST>;
+    using T = typename C::T;
+    constexpr int W = C::W;
+    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
+    const int64_t rl = blockIdx.x / (unsigned)chunks;
+    const int64_t row = row0 + rl;
+    const T *x = static_cast<const T *>(p.x0) + row * (int64_t)p.n;
+    const T *g = static_cast<const T *>(p.g0);
+    unsigned char *rec = static_cast<unsigned char *>(p.out0) +
+                         row * (int64_t)(p.n / 32) * 36;
+    const float r = inv[rl];
+    const int base = chunk * (MB * MVPT) + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < MVPT; ++k) {
+        const int i = base + k * MB;
+        const bool valid = i < p.nv;
+        float v[W], gv[W], y[W];
+        if (valid) {
+            C::load_nt(x, i, v);
+            C::load(g, i, gv);
+        } else {
+            zero(v);
+            zero(gv);
+        }
+#pragma unroll
+        for (int e = 0; e < W; ++e) y[e] = v[e] * r * gv[e];
+        q8_vector<W>(y, i, valid, rec);
+    }
+}
+
 __global__ void zero_kernel(unsigned int *p, int64_t words) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -851,6 +987,54 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 
 // Plain row tiles on the automatic menu also get the several-segment
 // launcher; the sweep-only shapes do not.
+template <int ST, int G, int VPT>
+hipError_t launch_q8(const RowArgs &p, int64_t row0, int64_t nrows,
+                     hipStream_t stream) {
+    constexpr int BLOCK = rowtile_block<G>();
+    constexpr int RPB = BLOCK / G;
+    const int64_t blocks = (nrows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((q8_kernel<ST, G, VPT>), dim3((unsigned int)blocks),
+                       dim3(BLOCK), 0, stream, p, row0, row0 + nrows);
+    return hipGetLastError();
+}
+
+template <int ST, int G, int VPT>
+hipError_t occupancy_q8(int *blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, q8_kernel<ST, G, VPT>, rowtile_block<G>(), 0);
+}
+
+template <int ST>
+hipError_t launch_multipass_q8(const RowArgs &p, float *scratch, int64_t row0,
+                               int64_t nrows, int chunks, hipStream_t stream) {
+    float *part = scratch;
+    float *inv = scratch + nrows * (int64_t)chunks;
+    const dim3 grid((unsigned int)(nrows * chunks));
+    hipLaunchKernelGGL(pass_sumsq<ST>, grid, dim3(MB), 0, stream, p, p.x0,
+                       row0, chunks, part);
+    hipLaunchKernelGGL(pass_combine, dim3((unsigned int)nrows), dim3(MB), 0,
+                       stream, (const float *)part, chunks, p.n, p.eps0, inv);
+    hipLaunchKernelGGL(pass_q8<ST>, grid, dim3(MB), 0, stream, p, row0, chunks,
+                       (const float *)inv);
+    return hipGetLastError();
+}
+
+#define SNR_Q8(ST, G, VPT)                                                  \
+    KernelEntry{OP_NORM_Q8, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,         \
+                rowtile_block<G>(), &launch_q8<ST, G, VPT>, nullptr,        \
+                &occupancy_q8<ST, G, VPT>, nullptr, nullptr}
+#define SNR_Q8_MULTI(ST)                                                    \
+    KernelEntry{OP_NORM_Q8, ST, Codec<ST>::W, KIND_MULTIPASS, MB, MVPT, MB, \
+                nullptr, nullptr, nullptr, &launch_multipass_q8<ST>, nullptr}
+// Q8_1 shapes: row groups of at least one block (8 lanes for f32, 4 for
+// 16-bit storage).
+#define SNR_Q8_SHAPES(ST)                                                   \
+    SNR_Q8(ST, 8, 4), SNR_Q8(ST, 16, 4), SNR_Q8(ST, 32, 4),                 \
+    SNR_Q8(ST, 128, 2), SNR_Q8(ST, 128, 8), SNR_Q8(ST, 256, 2),             \
+    SNR_Q8(ST, 256, 4), SNR_Q8(ST, 512, 2), SNR_Q8(ST, 512, 4),             \
+    SNR_Q8(ST, 1024, 1), SNR_Q8(ST, 1024, 2), SNR_Q8(ST, 1024, 4),          \
+    SNR_Q8(ST, 1024, 8), SNR_Q8_MULTI(ST)
+
 #define SNR_RT_M(OP, ST, G, VPT, M)                                         \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
                 rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
@@ -903,6 +1087,9 @@ const KernelEntry kTable[] = {
     SNR_AUTO_SHAPES(OP_NORM_ADD, ST_BF16), SNR_AUTO_SHAPES(OP_NORM_ADD, ST_F16),
     SNR_AUTO_SHAPES(OP_ADD_NORM, ST_F32), SNR_RT(OP_ADD_NORM, ST_F32, 1024, 16),
     SNR_AUTO_SHAPES(OP_ADD_NORM, ST_BF16), SNR_AUTO_SHAPES(OP_ADD_NORM, ST_F16),
+    SNR_Q8_SHAPES(ST_F32),               SNR_Q8(ST_F32, 1024, 16),
+    SNR_Q8_SHAPES(ST_BF16),              SNR_Q8(ST_BF16, 4, 4),
+    SNR_Q8_SHAPES(ST_F16),               SNR_Q8(ST_F16, 4, 4),
 };
 
 }  // namespace

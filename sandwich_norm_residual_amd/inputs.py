@@ -131,6 +131,17 @@ def _configs() -> dict:
                ((-2.0, 1.0),), segments=(52, 8)))
     add(Config("qknorm_prefill_bf16", "multi", 512 * 60, 128, "bf16", 332,
                (1e-5,), ((-2.0, 2.0),), segments=(512 * 52, 512 * 8)))
+    # RMSNorm into Q8_1 records (n a multiple of 32): a 4096-token batch at
+    # the model width, in f32 and bf16; one decode token at width 2560; and
+    # an edge sweep (zero rows and blocks, spikes, tiny rows)
+    add(Config("q8_4096x6656_f32", "q8", 4096, 6656, "f32", 341, (1e-5,),
+               ((-2.0, 1.0),)))
+    add(Config("q8_4096x6656_bf16", "q8", 4096, 6656, "bf16", 342, (1e-5,),
+               ((-2.0, 1.0),)))
+    add(Config("q8_1x2560_f32", "q8", 1, 2560, "f32", 343, (1e-5,),
+               ((-2.0, 1.0),)))
+    add(Config("q8_edge_256x6656_f32", "q8", 256, 6656, "f32", 344, (1e-5,),
+               ((-12.0, 6.0),), edge=True))
     for n in EDGE_NS:
         add(Config(f"edge_256x{n}_f32", "plain", 256, n, "f32", 500 + n,
                    (1e-5,), ((-12.0, 6.0),), edge=True))
@@ -183,7 +194,7 @@ def make_plain(cfg: Config, rows: int | None = None) -> dict:
     """Inputs for a plain RMSNorm configuration. ``rows`` may shrink the row
     count (the first rows of the same stream are NOT guaranteed identical to
     the full draw; a smaller row count is its own seeded input)."""
-    assert cfg.kind == "plain"
+    assert cfg.kind in ("plain", "q8")
     rows = cfg.rows if rows is None else rows
     rng = rng_for(cfg.seed)
     gamma = _gamma(rng, cfg.n)
@@ -245,7 +256,7 @@ def make_multi(cfg: Config) -> dict:
 
 def make(cfg_or_name, rows: int | None = None) -> dict:
     cfg = CONFIGS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
-    if cfg.kind == "plain":
+    if cfg.kind in ("plain", "q8"):
         return make_plain(cfg, rows)
     if cfg.kind == "tail":
         return make_tail(cfg, rows)

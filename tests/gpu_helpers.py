@@ -135,3 +135,51 @@ def run_add_norm(inp, sum_into=None, prefill=float("nan")):
     snr.add_then_norm(a, b, g, inp["eps"], sum_out=s, y_out=y)
     torch.cuda.synchronize()
     return host_f64(s), host_f64(y)
+
+
+# -- RMSNorm into Q8_1 records ---------------------------------------------
+# A code may differ from the oracle's by one only where the oracle's
+# unrounded t = v / d lies within Q8_TIE of a rounding boundary k + 1/2: the
+# GPU's t carries the f32 error of v and of d (a few units of 2^-24
+# relative, so at most about 1e-4 absolute for |t| <= 127).
+Q8_TIE = 1e-3
+
+
+def run_q8(inp):
+    """Q8_1 records of the inputs, as uint8 [rows, n / 32, 36] on the host."""
+    st = inp["dtype"]
+    x, g = dev(inp["x"], st), dev(inp["gamma"], st)
+    out = snr.rmsnorm_q8_1(x, g, inp["eps"])
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_q8(oracle, inp, blocks, label):
+    """Records against the oracle: s == 0; d within half an f16 unit of the
+    oracle's scale (relative, measured against at least the smallest f16
+    normal) plus f32 slack; zero blocks exactly zero; every code equal to
+    the oracle's except next to a rounding tie, where it is one of the two
+    neighbours. Returns (max relative d error, codes in the tie band)."""
+    x, g = f32(inp, "x"), f32(inp, "gamma")
+    _, d_o, t_o, q_o = oracle.rmsnorm_q8_1(x, g, inp["eps"])
+    rows, n = x.shape
+    assert blocks.shape == (rows, n // 32, 36) and blocks.dtype == np.uint8
+    d = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    s = blocks[..., 2:4].copy().view(np.uint16)[..., 0]
+    q = blocks[..., 4:36].copy().view(np.int8).reshape(rows, n)
+    assert np.all(s == 0), label
+    zero = d_o == 0
+    assert np.all(d[zero] == 0), (label, "zero block with d != 0")
+    derr = np.abs(d - d_o) / np.maximum(np.abs(d_o), 2.0 ** -14)
+    worst_d = float(derr[~zero].max()) if np.any(~zero) else 0.0
+    assert worst_d <= 2.0 ** -11 + 1e-5, (label, worst_d)
+    frac = np.abs(np.abs(t_o) - np.floor(np.abs(t_o)) - 0.5)
+    near = frac < Q8_TIE
+    dq = q.astype(np.int64) - q_o.astype(np.int64)
+    bad = (dq != 0) & ~near
+    assert not np.any(bad), (label, int(bad.sum()), "codes differ")
+    assert np.all(np.abs(dq[near]) <= 1), (label, "tie code off by > 1")
+    say(f"{label}: d err {worst_d:.3e}, {int(near.sum())} codes of "
+        f"{q.size} in the tie band, {int((dq != 0).sum())} differ; shape "
+        f"{snr.last_shape()}")
+    return worst_d, int(near.sum())

@@ -231,3 +231,20 @@ def test_multi_argument_errors(L):
         _lib.SNR_ERR_ALIAS                          # a gain inside an output
     assert call([Seg(0, 0, 0, 0, 1e-5), Seg(0, 0, 0, 0, 1e-5)]) == \
         _lib.SNR_OK                                 # nothing to do
+
+
+def test_q8_1_argument_errors(L):
+    f = _lib.rmsnorm_q8_1
+    assert f(BASE, GAM, 1e-5, 4, 48, 0, OUT, 0) == _lib.SNR_ERR_SHAPE  # 32∤n
+    assert f(BASE, GAM, 1e-5, 4, 16, 0, OUT, 0) == _lib.SNR_ERR_SHAPE
+    assert f(BASE, GAM, 1e-5, 4, 64, 3, OUT, 0) == _lib.SNR_ERR_DTYPE
+    assert f(BASE, GAM, 0.0, 4, 64, 0, OUT, 0) == _lib.SNR_ERR_EPS
+    assert f(BASE, 0, 1e-5, 4, 64, 0, OUT, 0) == _lib.SNR_ERR_NULL
+    assert f(BASE, GAM, 1e-5, 4, 64, 0, 0, 0) == _lib.SNR_ERR_NULL
+    assert f(BASE, GAM, 1e-5, 4, 64, 0, OUT + 2, 0) == _lib.SNR_ERR_ALIGN
+    assert f(BASE + 2, GAM, 1e-5, 4, 64, 0, OUT, 0) == _lib.SNR_ERR_ALIGN
+    assert f(BASE, GAM, 1e-5, 4, 64, 0, BASE + 64, 0) == \
+        _lib.SNR_ERR_ALIAS                          # records over x
+    assert f(BASE, GAM, 1e-5, 4, 64, 0, GAM - 16, 0) == \
+        _lib.SNR_ERR_ALIAS                          # records over gamma
+    assert f(0, 0, 1e-5, 0, 64, 0, 0, 0) == _lib.SNR_OK

@@ -1,0 +1,115 @@
+"""GPU parity of RMSNorm into Q8_1 records against the f64 oracle: every
+compiled dispatch shape, the full-size workloads, ragged and edge rows, and
+all three storage types."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import sandwich_norm_residual_amd as snr  # noqa: E402
+from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
+from gpu_helpers import check_q8, dev, run_q8, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+VEC = {"f32": 4, "bf16": 8, "f16": 8}
+Q8_ROWTILE = [(8, 4), (16, 4), (32, 4), (128, 2), (128, 8), (256, 2),
+              (256, 4), (512, 2), (512, 4), (1024, 1), (1024, 2), (1024, 4),
+              (1024, 8)]
+
+
+def _forced_cases():
+    cases = []
+    for st in ("f32", "bf16", "f16"):
+        shapes = [("rowtile", g, v) for g, v in Q8_ROWTILE]
+        if st == "f32":
+            shapes.append(("rowtile", 1024, 16))
+        else:
+            shapes.append(("rowtile", 4, 4))
+        shapes.append(("multipass", 0, 8))
+        cases += [(st, k, g, v) for k, g, v in shapes]
+    return cases
+
+
+@pytest.mark.parametrize("case", _forced_cases(),
+                         ids=lambda c: "{}-{}-g{}-v{}".format(*c))
+def test_forced_shape(oracle, case):
+    """Each compiled shape on rows that fill its tile only partly (the row's
+    vector count is the largest whole number of 32-element blocks below
+    g * vpt - g / 2)."""
+    st, kind, g, v = case
+    w = VEC[st]
+    bv = 32 // w
+    if kind == "rowtile":
+        nv = max(bv, (g * v - g // 2) // bv * bv)
+    else:
+        nv = 2 * 2048 + 8          # three chunks of 256 x 8 vectors
+    n = nv * w
+    rows = 19
+    label = f"q8-{st}-{kind}-g{g}-v{v}-n{n}"
+    say(f"forced {label} rows={rows}")
+    inp = gen.random_plain(rows, n, 26000 + g * 7 + v + n, dtype=st)
+    with snr.forced_shape(kind, g, v):
+        blocks = run_q8(inp)
+        shape = snr.last_shape()
+    check_q8(oracle, inp, blocks, label)
+    if kind == "rowtile":
+        assert shape == f"rowtile:{g}:{v}:{w}", shape
+    else:
+        assert shape.startswith(f"multipass:256:8:{w}:3"), shape
+
+
+@pytest.mark.parametrize("name", ["q8_4096x6656_f32", "q8_4096x6656_bf16",
+                                  "q8_1x2560_f32", "q8_edge_256x6656_f32"])
+def test_workload_full_size(oracle, name):
+    cfg = gen.CONFIGS[name]
+    say(f"workload {name}")
+    inp = gen.make(cfg)
+    _, near = check_q8(oracle, inp, run_q8(inp), name)
+    # the tie band is a sliver: nearly every code is compared exactly
+    assert near <= 1e-2 * cfg.rows * cfg.n
+
+
+@pytest.mark.parametrize("st", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [32, 64, 96, 2560, 6656, 65536, 65536 + 32,
+                               4 * 65536])
+def test_widths_auto(oracle, st, n):
+    """Automatic shape choice from one block up to rows the multi-pass
+    kernels take."""
+    rows = 13
+    say(f"q8 auto {st} n={n}")
+    inp = gen.random_plain(rows, n, 27000 + n, dtype=st)
+    check_q8(oracle, inp, run_q8(inp), f"q8-auto-{st}-{n}")
+
+
+def test_zero_rows_and_blocks(oracle):
+    """An all-zero row, and zero blocks inside a row, encode as d = 0 and
+    q = 0; the row's other blocks are unaffected."""
+    rows, n = 4, 256
+    inp = gen.random_plain(rows, n, 28000)
+    inp["x"][0] = 0.0
+    inp["x"][1, 32:96] = 0.0
+    inp["x"][2, :] = 0.0
+    inp["x"][2, 200] = -7.0
+    blocks = run_q8(inp)
+    check_q8(oracle, inp, blocks, "q8-zero-blocks")
+    assert not blocks[0].any()
+    assert not blocks[1, 1:3].any()
+    assert not blocks[2, [0, 1, 2, 3, 4, 5, 7]].any()
+    d, s, q = snr.q8_1_fields(torch.from_numpy(blocks))
+    assert q[2, 6, 200 - 192].item() == -127
+
+
+def test_rows_zero_and_out_argument(oracle):
+    x = torch.empty((0, 64), device="cuda:0")
+    g = torch.ones(64, device="cuda:0")
+    assert snr.rmsnorm_q8_1(x, g, 1e-5).shape == (0, 2, 36)
+    inp = gen.random_plain(5, 128, 29000)
+    xs, gs = dev(inp["x"], "f32"), dev(inp["gamma"], "f32")
+    out = torch.full((5, 4, 36), 0xAB, dtype=torch.uint8, device="cuda:0")
+    r = snr.rmsnorm_q8_1(xs, gs, 1e-5, out=out)
+    assert r is out
+    check_q8(oracle, inp, out.cpu().numpy(), "q8-out-arg")
+    with pytest.raises(ValueError):
+        snr.rmsnorm_q8_1(xs[:, :100].contiguous(), gs[:100].contiguous(),
+                         1e-5)
