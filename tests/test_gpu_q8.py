@@ -113,3 +113,23 @@ def test_rows_zero_and_out_argument(oracle):
     with pytest.raises(ValueError):
         snr.rmsnorm_q8_1(xs[:, :100].contiguous(), gs[:100].contiguous(),
                          1e-5)
+
+
+def test_tiny_blocks_and_subnormal_inputs(oracle):
+    """Blocks whose scale d is an f32 subnormal (amax ~ 1e-37) and rows of
+    subnormal inputs whose normalised values are normal: the quotient
+    v / d must stay finite and accurate (no reciprocal of a subnormal)."""
+    rng = gen.rng_for(28100)
+    rows, n = 4, 256
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    x[0, 0:32] *= np.float32(1e-37)      # normalised block ~1e-37: d subnormal
+    x[1, 64:96] *= np.float32(3e-36)
+    x[2] *= np.float32(1e-40)            # subnormal inputs, eps dominates
+    x[3, :] = 0.0
+    x[3, 5] = np.float32(1e-44)          # one subnormal element
+    g = (1.0 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    inp = {"x": x, "gamma": g, "eps": 1e-5, "dtype": "f32"}
+    blocks = run_q8(inp)
+    check_q8(oracle, inp, blocks, "q8-tiny")
+    d, s, q = snr.q8_1_fields(torch.from_numpy(blocks))
+    assert int(q[0, 0].abs().max()) == 127      # the block's own scale
