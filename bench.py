@@ -11,10 +11,10 @@ Prints ONE JSON line on stdout: achieved HBM GB/s from algorithmic bytes
 dominant kernel's roofline (per-launch time from HIP events on the launch
 stream) and the f64 oracle's throughput on the host cores.
 
-Inputs are resident in HBM before timing starts. Three (default) rotating
-sets of input/output buffers, together larger than twice the 256 MB
-Infinity Cache, keep one launch's inputs from being served by the cache the
-previous launch warmed.
+Inputs are resident in HBM before timing starts. Rotating sets of
+input/output buffers (at least three, and together at least 1 GiB of step
+traffic, four times the 256 MB Infinity Cache; at most 64) keep one launch's
+inputs from being served by the cache the previous launches warmed.
 """
 from __future__ import annotations
 
@@ -54,14 +54,23 @@ def algorithmic_bytes(cfg) -> int:
     return streams * cfg.rows * cfg.n * es + gains * cfg.n * es
 
 
-def kernel_source_digest() -> str:
-    """sha256 of the kernel source; counters recorded for another source are
-    not reported."""
+def kernel_sources(cfg) -> list:
+    """The source files the workload's kernels are built from."""
+    csrc = os.path.join(ROOT, "sandwich_norm_residual_amd", "csrc")
+    main = "snr_q8.hip" if cfg.kind == "q8" else "snr_kernels.hip"
+    return [os.path.join(csrc, f)
+            for f in ("snr_internal.h", "snr_device.h", main)]
+
+
+def kernel_source_digest(cfg) -> str:
+    """sha256 over the workload's kernel sources; counters recorded for other
+    sources are not reported."""
     import hashlib
-    path = os.path.join(ROOT, "sandwich_norm_residual_amd", "csrc",
-                        "snr_kernels.hip")
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in kernel_sources(cfg):
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(cfg, shape):
@@ -78,7 +87,7 @@ def measured_traffic(cfg, shape):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if (kv.get("kernel_source_sha256") != kernel_source_digest() or
+    if (kv.get("kernel_source_sha256") != kernel_source_digest(cfg) or
             kv.get("dispatch_shape") != shape):
         return None
     return float(kv["traffic_bytes_per_launch"])
@@ -237,8 +246,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=None,
                     help="workload name (default: the 4096x6656 f32 tail)")
-    ap.add_argument("--sets", type=int, default=3,
-                    help="rotating buffer sets (defeat the Infinity Cache)")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="rotating buffer sets (default: at least 3 and 1 GiB "
+                         "of step traffic together, at most 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle CPU baseline")
@@ -252,9 +262,10 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (rows shard across GPUs with no communication; see the "
-              "design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(rows are independent, so a batch would shard across GPUs by "
+              "rows with no communication). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -270,9 +281,10 @@ def main() -> int:
     log(f"workload {cfg.name}: rows={cfg.rows} n={cfg.n} {cfg.dtype} "
         f"seed={cfg.seed}")
     inp = gen.make(cfg)
-    sets = make_device_sets(cfg, inp, args.sets, torch)
-    stream = torch.cuda.Stream()   # default priority
     nbytes = algorithmic_bytes(cfg)
+    nsets = args.sets or min(64, max(3, -(-(1 << 30) // nbytes)))
+    sets = make_device_sets(cfg, inp, nsets, torch)
+    stream = torch.cuda.Stream()   # default priority
 
     step = make_step(cfg, inp, sets, snr, args.separate_launches)
 

@@ -150,10 +150,16 @@ struct Choice {
     int chunks = 0;  // split only
 };
 
+// The compiled kernels of an operation: RMSNorm into Q8_1 records has its
+// own source and table.
+const KernelEntry *table_for(int op, int *count) {
+    return op == OP_NORM_Q8 ? q8_kernel_table(count) : kernel_table(count);
+}
+
 const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
                               int vpt) {
     int count = 0;
-    const KernelEntry *t = kernel_table(&count);
+    const KernelEntry *t = table_for(op, &count);
     for (int i = 0; i < count; ++i)
         if (t[i].op == op && t[i].storage == st && t[i].width == w &&
             t[i].kind == kind && (kind != KIND_ROWTILE || t[i].g == g) &&
@@ -201,7 +207,7 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
     int g = 64;
     while (g < 1024 && 2LL * g < nv) g *= 2;
     int count = 0;
-    const KernelEntry *t = kernel_table(&count);
+    const KernelEntry *t = table_for(op, &count);
     const KernelEntry *best = nullptr;
     for (int i = 0; i < count; ++i) {
         const KernelEntry &e = t[i];

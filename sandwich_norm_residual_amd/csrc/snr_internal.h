@@ -104,8 +104,10 @@ struct KernelEntry {
     MultiLaunch multi;   // several segments in one launch (row tile only)
 };
 
-// The table of compiled kernels (defined in snr_kernels.hip).
+// The tables of compiled kernels: RMSNorm, the tail and its halves
+// (snr_kernels.hip), and RMSNorm into Q8_1 records (snr_q8.hip).
 const KernelEntry *kernel_table(int *count);
+const KernelEntry *q8_kernel_table(int *count);
 
 // Zero `words` 32-bit words with a kernel (used instead of a memset so that
 // the call can also be recorded into a HIP graph).
