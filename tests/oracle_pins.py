@@ -554,6 +554,24 @@ def pin_q8_properties(O):
         assert np.array_equal(q[ok], q2[ok])
 
 
+def pin_q8_ties_to_even(O):
+    """Exact ties: x = [254, 1, 3, 5, 7, -1, -3, -5, -7, 200, 160, 28, 2,
+    0 x 19], gamma = 1, eps = 1e-30. Sum x^2 = 131072 = 32 * 4096, so
+    mean + eps rounds to 4096 and rms = 64 exactly; y = x / 64 exactly,
+    amax = 254 / 64 and d = amax / 127 = 1 / 32 exactly, so t = x / 2
+    exactly and the odd entries are true ties k + 1/2. Round half to even
+    (WGSL round) gives 0, 2, 2, 4 for 0.5, 1.5, 2.5, 3.5; half away from
+    zero would give 1, 2, 3, 4."""
+    vals = [254, 1, 3, 5, 7, -1, -3, -5, -7, 200, 160, 28, 2] + [0] * 19
+    assert sum(v * v for v in vals) == 32 * 4096
+    x = np.array([vals], F32)
+    y, d, t, q = O.rmsnorm_q8_1(x, np.ones(32, F32), 1e-30)
+    assert d[0, 0] == 1.0 / 32.0
+    assert np.array_equal(t[0], np.array(vals, np.float64) / 2.0)
+    want = [127, 0, 2, 2, 4, 0, -2, -2, -4, 100, 80, 14, 1] + [0] * 19
+    assert q[0].tolist() == want
+
+
 def pin_q8_decimal(O):
     """Exact decimal arithmetic on short rows: codes agree away from ties,
     scales to 1e-14."""
@@ -605,5 +623,6 @@ ALL_PINS = [
     pin_decimal_halves,
     pin_q8_closed_form,
     pin_q8_properties,
+    pin_q8_ties_to_even,
     pin_q8_decimal,
 ]

@@ -54,6 +54,8 @@ MUTANTS = {
     "q8_divides_by_128": ("const double db = amax / 127.0;",
                           "const double db = amax / 128.0;"),
     "q8_truncates": ("double r = nearbyint(t[j]);", "double r = trunc(t[j]);"),
+    "q8_rounds_half_away": ("double r = nearbyint(t[j]);",
+                            "double r = round(t[j]);"),
     "q8_row_amax": ("if (fabs(yi[b * 32 + l]) > amax)\n                    amax = fabs(yi[b * 32 + l]);",
                     "if (fabs(yi[l]) > amax)\n                    amax = fabs(yi[l]);"),
     "q8_before_gain": ("t[j] = yi[b * 32 + l] / db;",
