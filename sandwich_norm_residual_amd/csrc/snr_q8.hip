@@ -43,17 +43,34 @@ __device__ __forceinline__ unsigned int group_max_bits(unsigned int v) {
     return v;
 }
 
+// 127 / m for m in [0.5, 1): the hardware reciprocal refined by one Newton
+// step, then the quotient corrected by its remainder, which a fused
+// multiply-add computes exactly (Markstein's scheme). With the reciprocal
+// anywhere within one unit of 1/m this gives the correctly rounded quotient
+// (checked in exact arithmetic by the host tests), and the exact quotient
+// where it is representable (m = 1/2 and 127/128), so an exact tie stays a
+// tie. With m bounded away from zero, infinity and the subnormals, none of
+// the scaling and special-case steps of a general division apply.
+__device__ __forceinline__ float q8_quotient127(float m) {
+    float r = __builtin_amdgcn_rcpf(m);
+    r = fmaf(fmaf(-m, r, 1.0f), r, r);
+    const float q = 127.0f * r;
+    return fmaf(fmaf(-m, q, 127.0f), r, q);
+}
+
 // The codes of one lane's W values z = x * gamma (all lanes of the wavefront
 // call it: the block's max|z| is a cross-lane max), packed into W / 4 words;
 // returns the block's max|z|.
 // t = 127 z / max|z| is formed as (z 2^-e) * (127 / (max|z| 2^-e)) with e
 // the binary exponent of max|z|: the power-of-two scalings are exact, the
-// reciprocal is of a value in [0.5, 1) (so nothing overflows for any
-// max|z| > 0, subnormal included), and t is within a few f32 units of the
-// exact quotient, which moves a code only next to a rounding tie. Adding
-// 1.5 * 2^23 in the same fused multiply-add rounds t to the nearest integer,
-// ties to even, and leaves it in the sum's low bits (|t| <= 127 up to
-// rounding, so the int8 clamp never binds); the code is the low byte.
+// divisor lies in [0.5, 1) (so nothing overflows for any max|z| > 0,
+// subnormal included), and the quotient 127 / m is correctly rounded. The
+// fused multiply-add with 1.5 * 2^23 then rounds the exact product to the
+// nearest integer, ties to even, leaving it in the sum's low bits (|t| <=
+// 127 up to rounding, so the int8 clamp never binds); the code is the low
+// byte. So a code is round-half-even of the exact quotient whenever 127 / m
+// is exact (an exact tie stays a tie), and otherwise differs from it only
+// within about 127 * 2^-24 of a tie.
 template <int W>
 __device__ __forceinline__ float q8_codes(const float (&z)[W],
                                           unsigned int (&words)[W / 4]) {
@@ -63,8 +80,7 @@ __device__ __forceinline__ float q8_codes(const float (&z)[W],
     for (int e = 0; e < W; ++e) m = max(m, __float_as_uint(fabsf(z[e])));
     const float amax = __uint_as_float(group_max_bits<BV>(m));
     const int ex = __builtin_amdgcn_frexp_expf(amax);
-    const float s =
-        amax > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(ldexpf(amax, -ex)) : 0.0f;
+    const float s = amax > 0.0f ? q8_quotient127(ldexpf(amax, -ex)) : 0.0f;
     unsigned int c[W];
 #pragma unroll
     for (int e = 0; e < W; ++e)
@@ -153,10 +169,7 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     // (about one f32 unit) replaces IEEE square root and division: a shorter
     // chain between a row's reduction and its stores.
     const float inv_n = 1.0f / (float)p.n;
-    auto inverse_rms = [&](const float (&v)[VPT][W], float *slot) {
-        float s = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) s += sumsq<W>(v[k]);
+    auto inverse_rms = [&](float s, float *slot) {
         return __builtin_amdgcn_rsqf(fmaf(row_total<G>(s, slot), inv_n, p.eps0));
     };
 
@@ -213,27 +226,29 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
                 raw[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off_x[k], 0,
                                                               kNonTemporal);
         };
-        auto quant_rows = [&](const u32x4 (&raw)[VPT], const float (&gv)[VPT][W],
+        auto quant_rows = [&](const u32x4 (&raw)[VPT], const u32x4 (&graw)[VPT],
                               int64_t b, float *slot) {
-            float v[VPT][W], amax[VPT];
-#pragma unroll
-            for (int k = 0; k < VPT; ++k)
-                C::decode(__builtin_bit_cast(typename C::vec, raw[k]), v[k]);
             const auto rs = buffer_of(out + (b < row_end ? b : first) * rec_row,
                                       live_rows(b) * rec_row);
-            // The codes do not depend on the row's reduction, so they are
-            // computed while it is under way; a record's codes and header
-            // are stored together afterwards (written apart, the two parts
-            // of a record's cache line leave the cache separately).
+            // The codes do not depend on the row's reduction, so one pass
+            // over the vectors forms each vector's codes and its share of
+            // the sum of squares (the decoded row is never held whole); a
+            // record's codes and header are stored together after the
+            // reduction (written apart, the two parts of a record's cache
+            // line leave the cache separately).
             unsigned int words[VPT][W / 4];
+            float amax[VPT], s = 0.0f;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
-                float z[W];
+                float v[W], gk[W], z[W];
+                C::decode(__builtin_bit_cast(typename C::vec, raw[k]), v);
+                C::decode(__builtin_bit_cast(typename C::vec, graw[k]), gk);
+                s += sumsq<W>(v);
 #pragma unroll
-                for (int e = 0; e < W; ++e) z[e] = v[k][e] * gv[k][e];
+                for (int e = 0; e < W; ++e) z[e] = v[e] * gk[e];
                 amax[k] = q8_codes<W>(z, words[k]);
             }
-            const float inv = inverse_rms(v, slot);
+            const float inv = inverse_rms(s, slot);
             if constexpr (STAGE) {
                 // every lane of a record writes its header (the same value)
                 const int j = lane / BV;
@@ -290,11 +305,15 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
         // and it then waits for all of them.
         constexpr int NB = PD + 1;
         const int64_t trips = (row_end - first + stride - 1) / stride;
-        float gv[VPT][W];
+        // the gains stay in registers as stored (half the registers for
+        // 16-bit storage) and are decoded where used
+        u32x4 gv[VPT];
+        const auto rg = buffer_of(g, row_bytes);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int i = k * G + sub;
-            C::load(g, i < nv ? i : nv - 1, gv[k]);
+            gv[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                rg, i < nv ? 16u * i : kOutOfRange, 0, 0);
         }
         u32x4 buf[NB][VPT];
 #pragma unroll
@@ -339,7 +358,10 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
             const int i = k * G + sub;
             if (live && i < nv) C::load_nt(xr, i, v[k]); else zero(v[k]);
         }
-        const float inv = inverse_rms(v, red[0]);
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) s += sumsq<W>(v[k]);
+        const float inv = inverse_rms(s, red[0]);
         unsigned char *rec = out + (live ? row : 0) * rec_row;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {

@@ -133,3 +133,21 @@ def test_tiny_blocks_and_subnormal_inputs(oracle):
     check_q8(oracle, inp, blocks, "q8-tiny")
     d, s, q = snr.q8_1_fields(torch.from_numpy(blocks))
     assert int(q[0, 0].abs().max()) == 127      # the block's own scale
+
+
+def test_exact_ties_round_to_even(oracle):
+    """A block whose quotients x / d are exact ties (rms = 64 and d = 1/32
+    exactly, t = x / 2): the codes are round-half-even of the exact
+    quotient, equal to the oracle's with no tie band."""
+    vals = [254, 1, 3, 5, 7, -1, -3, -5, -7, 200, 160, 28, 2] + [0] * 19
+    x = np.array([vals, [-v for v in vals]], np.float32)
+    inp = {"x": x, "gamma": np.ones(32, np.float32), "eps": 1e-30,
+           "dtype": "f32"}
+    blocks = run_q8(inp)
+    d, s, q = snr.q8_1_fields(torch.from_numpy(blocks))
+    want = [127, 0, 2, 2, 4, 0, -2, -2, -4, 100, 80, 14, 1] + [0] * 19
+    assert q[0, 0].tolist() == want
+    assert q[1, 0].tolist() == [-v for v in want]
+    assert float(d[0, 0]) == 1.0 / 32.0 and float(d[1, 0]) == 1.0 / 32.0
+    _, _, _, qo = oracle.rmsnorm_q8_1(x, inp["gamma"], inp["eps"])
+    assert np.array_equal(q.reshape(2, 32).numpy(), qo)
