@@ -212,6 +212,19 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
             O.add_then_norm(f["a"][lo:hi], f["b"][lo:hi], f["gamma"],
                             inp["eps"])
 
+    # one core first (about a third of the budget, rows in slices), then
+    # every core
+    t1 = time.perf_counter()
+    rows1 = 0
+    while time.perf_counter() - t1 < seconds / 3:
+        for b in bounds:
+            one(b)
+            rows1 += b[1] - b[0]
+            if time.perf_counter() - t1 >= seconds / 3:
+                break
+    dt1 = time.perf_counter() - t1
+    gbs1 = algorithmic_bytes(cfg) * rows1 / rows / dt1 / 1e9
+
     passes = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(len(bounds)) as ex:
@@ -233,10 +246,13 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
         pass
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": len(bounds),
             "kind": "oracle",
+            "single_core_value": round(gbs1, 3),
             "sample": (f"{passes} full passes over {cfg.name} "
                        f"({rows} rows) in {dt:.1f} s, scalar f64 C oracle, "
                        f"rows split over {len(bounds)} threads; "
-                       f"rows/s {rows * passes / dt:.4g}; cpu: {model}")}
+                       f"rows/s {rows * passes / dt:.4g}; one core: "
+                       f"{rows1} rows in {dt1:.1f} s, {gbs1:.3g} GB/s, "
+                       f"rows/s {rows1 / dt1:.4g}; cpu: {model}")}
 
 
 def main() -> int:
