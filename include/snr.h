@@ -261,11 +261,20 @@ SNR_API int snr_last_hip_error(void);
  *                             device memory (reads the row twice; the tail
  *                             also re-reads h). Chosen automatically only
  *                             when the split shape cannot hold the row.
+ *          SNR_SHAPE_PERSIST  the row tile (g >= 128 lanes, one row per
+ *                             workgroup) on a persistent grid that loads the
+ *                             next row while reducing the current one; same
+ *                             arithmetic and results as SNR_SHAPE_ROWTILE
+ *                             with the same g and vpt. Only for rows with n
+ *                             a multiple of the vector width (4 f32, 8
+ *                             16-bit), and not for rmsnorm_q8_1 (whose row
+ *                             tiles are persistent already).
  * snr_force_shape applies to subsequent calls on the calling thread until it
  * is called again with SNR_SHAPE_AUTO. A forced shape that cannot hold the
  * row (g * vpt loads < row length) or that has no compiled kernel returns
- * SNR_ERR_SHAPE from the call. snr_last_shape writes "rowtile:g:vpt:width"
- * or "split:256:vpt:width:chunks" or "multipass:256:8:width:chunks" (width =
+ * SNR_ERR_SHAPE from the call. snr_last_shape writes "rowtile:g:vpt:width",
+ * "persist:g:vpt:width", "split:256:vpt:width:chunks" or
+ * "multipass:256:8:width:chunks" (width =
  * elements per 128-bit vector) of
  * the calling thread's most recent successful launch into buf
  * (NUL-terminated).
@@ -274,7 +283,8 @@ enum {
     SNR_SHAPE_AUTO = 0,
     SNR_SHAPE_ROWTILE = 1,
     SNR_SHAPE_SPLIT = 2,
-    SNR_SHAPE_MULTIPASS = 3
+    SNR_SHAPE_MULTIPASS = 3,
+    SNR_SHAPE_PERSIST = 4
 };
 SNR_API int snr_force_shape(int kind, int g, int vpt);
 SNR_API int snr_last_shape(char *buf, int len);

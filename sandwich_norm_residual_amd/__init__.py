@@ -291,10 +291,11 @@ def q8_1_fields(blocks):
 
 @contextlib.contextmanager
 def forced_shape(kind: str, g: int = 0, vpt: int = 0):
-    """Force a dispatch shape ("rowtile", "split" or "multipass") for calls
-    made on this thread inside the block (diagnostics and tests)."""
+    """Force a dispatch shape ("rowtile", "persist", "split" or "multipass")
+    for calls made on this thread inside the block (diagnostics and tests)."""
     code = {"auto": _lib.SHAPE_AUTO, "rowtile": _lib.SHAPE_ROWTILE,
-            "split": _lib.SHAPE_SPLIT, "multipass": _lib.SHAPE_MULTIPASS}[kind]
+            "split": _lib.SHAPE_SPLIT, "multipass": _lib.SHAPE_MULTIPASS,
+            "persist": _lib.SHAPE_PERSIST}[kind]
     _lib.force_shape(code, g, vpt)
     try:
         yield

@@ -31,6 +31,7 @@ SHAPE_AUTO = 0
 SHAPE_ROWTILE = 1
 SHAPE_SPLIT = 2
 SHAPE_MULTIPASS = 3
+SHAPE_PERSIST = 4
 
 MAX_SEGMENTS = 8
 

@@ -150,20 +150,22 @@ struct Choice {
     int chunks = 0;  // split only
 };
 
-// The compiled kernels of an operation: RMSNorm into Q8_1 records has its
-// own source and table.
-const KernelEntry *table_for(int op, int *count) {
-    return op == OP_NORM_Q8 ? q8_kernel_table(count) : kernel_table(count);
+// The compiled kernels of an operation and kind: RMSNorm into Q8_1 records
+// and the persistent row tiles have their own sources and tables.
+const KernelEntry *table_for(int op, int kind, int *count) {
+    if (op == OP_NORM_Q8) return q8_kernel_table(count);
+    if (kind == KIND_PERSIST) return persist_kernel_table(count);
+    return kernel_table(count);
 }
 
 const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
                               int vpt) {
     int count = 0;
-    const KernelEntry *t = table_for(op, &count);
+    const KernelEntry *t = table_for(op, kind, &count);
+    const bool by_g = kind == KIND_ROWTILE || kind == KIND_PERSIST;
     for (int i = 0; i < count; ++i)
         if (t[i].op == op && t[i].storage == st && t[i].width == w &&
-            t[i].kind == kind && (kind != KIND_ROWTILE || t[i].g == g) &&
-            t[i].vpt == vpt)
+            t[i].kind == kind && (!by_g || t[i].g == g) && t[i].vpt == vpt)
             return &t[i];
     return nullptr;
 }
@@ -174,7 +176,13 @@ int split_chunks(const KernelEntry *k, int64_t nv) {
     return (int)(c > 0 ? c : 1);  // a row of only remainder elements
 }
 
-int choose(int op, int st, int w, int64_t nv, Choice *c) {
+int choose(int op, int st, int w, int64_t nv, int rem, Choice *c) {
+    if (t_force_kind == SNR_SHAPE_PERSIST) {
+        if (op == OP_NORM_Q8 || rem != 0) return SNR_ERR_SHAPE;
+        c->k = find_entry(op, st, w, KIND_PERSIST, t_force_g, t_force_vpt);
+        if (!c->k || (int64_t)c->k->g * c->k->vpt < nv) return SNR_ERR_SHAPE;
+        return SNR_OK;
+    }
     if (t_force_kind == SNR_SHAPE_ROWTILE) {
         c->k = find_entry(op, st, w, KIND_ROWTILE, t_force_g, t_force_vpt);
         if (!c->k || (int64_t)c->k->g * c->k->vpt < nv) return SNR_ERR_SHAPE;
@@ -207,7 +215,7 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
     int g = 64;
     while (g < 1024 && 2LL * g < nv) g *= 2;
     int count = 0;
-    const KernelEntry *t = table_for(op, &count);
+    const KernelEntry *t = table_for(op, KIND_ROWTILE, &count);
     const KernelEntry *best = nullptr;
     for (int i = 0; i < count; ++i) {
         const KernelEntry &e = t[i];
@@ -226,6 +234,18 @@ int choose(int op, int st, int w, int64_t nv, Choice *c) {
         return SNR_OK;
     }
     c->k = best;
+    // The persistent form of the same tile (loads of the next row in flight
+    // through this row's reductions) measured faster for the 16-bit tail
+    // and its halves with 512 or more lanes per row (4096 x 6656: bf16 tail
+    // 43.1 -> 40.9 us, norm_then_add 32.4 -> 30.0 us) and slower for f32,
+    // for the plain norm and for smaller groups, whose rows are shorter than
+    // the loop's fixed cost; it needs rows without a ragged end.
+    if (st != ST_F32 && rem == 0 && best->g >= 512 &&
+        (op == OP_TAIL || op == OP_NORM_ADD || op == OP_ADD_NORM)) {
+        const KernelEntry *pk =
+            find_entry(op, st, w, KIND_PERSIST, best->g, best->vpt);
+        if (pk) c->k = pk;
+    }
     return SNR_OK;
 }
 
@@ -246,7 +266,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     a.nv = (int32_t)(a.n / w);
     a.rem = (int32_t)(a.n % w);
     Choice c;
-    rc = choose(op, st, w, a.nv, &c);
+    rc = choose(op, st, w, a.nv, a.rem, &c);
     if (rc != SNR_OK) return rc;
     const KernelEntry *k = c.k;
 
@@ -267,7 +287,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         }
     }
 
-    if (k->kind == KIND_ROWTILE) {
+    if (k->kind == KIND_ROWTILE || k->kind == KIND_PERSIST) {
         const int rpb = k->block / k->g;
         const int64_t max_blocks = (int64_t)(UINT32_MAX / (uint32_t)k->block);
         const int64_t step = max_blocks * rpb;
@@ -318,9 +338,10 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             if (e != hipSuccess) return hip_fail(e);
         }
     }
-    if (k->kind == KIND_ROWTILE)
-        std::snprintf(t_last_shape, sizeof t_last_shape, "rowtile:%d:%d:%d",
-                      k->g, k->vpt, w);
+    if (k->kind == KIND_ROWTILE || k->kind == KIND_PERSIST)
+        std::snprintf(t_last_shape, sizeof t_last_shape, "%s:%d:%d:%d",
+                      k->kind == KIND_ROWTILE ? "rowtile" : "persist", k->g,
+                      k->vpt, w);
     else
         std::snprintf(t_last_shape, sizeof t_last_shape, "%s:%d:%d:%d:%d",
                       k->kind == KIND_SPLIT ? "split" : "multipass", k->g,
@@ -574,7 +595,7 @@ int rmsnorm_fwd_multi(const snr_segment *segs, int count, int64_t n,
     if (rc != SNR_OK) return rc;
     const int w = (int)(16 / es);
     Choice c;
-    rc = choose(OP_PLAIN, st, w, n / w, &c);
+    rc = choose(OP_PLAIN, st, w, n / w, (int)(n % w), &c);
     if (rc != SNR_OK) return rc;
     if (c.k->kind != KIND_ROWTILE || !c.k->multi) {
         // rows too wide for one register tile (or a forced shape without a
@@ -638,7 +659,8 @@ int snr_last_hip_error(void) { return t_last_hip_error; }
 
 int snr_force_shape(int kind, int g, int vpt) {
     if (kind != SNR_SHAPE_AUTO && kind != SNR_SHAPE_ROWTILE &&
-        kind != SNR_SHAPE_SPLIT && kind != SNR_SHAPE_MULTIPASS)
+        kind != SNR_SHAPE_SPLIT && kind != SNR_SHAPE_MULTIPASS &&
+        kind != SNR_SHAPE_PERSIST)
         return SNR_ERR_SHAPE;
     t_force_kind = kind;
     t_force_g = g;

@@ -39,6 +39,9 @@ struct Codec<ST_F32> {
     __device__ static void decode(const vec q, float (&v)[4]) {
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
+    __device__ static vec encode(const float (&v)[4]) {
+        return vec{v[0], v[1], v[2], v[3]};
+    }
     __device__ static void load_nt(const T *row, int i, float (&v)[4]) {
         const vec q = __builtin_nontemporal_load(
             reinterpret_cast<const vec *>(row) + i);
@@ -97,8 +100,17 @@ struct F16Bits {
     __device__ static float hi(unsigned int w) {
         return (float)__builtin_bit_cast(f16x2, w).y;
     }
+    // A stored value is the f16 rounding of the f32 result. The empty asm
+    // makes the f32 value opaque, so the compiler cannot fuse the operation
+    // that produced it with the conversion (v_fma_mix*/v_mad_mix* round once,
+    // straight to f16); otherwise kernels would round differently wherever
+    // it happened to fuse.
+    __device__ static float settle(float v) {
+        __asm__("" : "+v"(v));
+        return v;
+    }
     __device__ static unsigned int pack(float a, float b) {
-        const f32x2 f = {a, b};
+        const f32x2 f = {settle(a), settle(b)};
         return __builtin_bit_cast(unsigned int,
                                   __builtin_convertvector(f, f16x2));
     }
@@ -106,7 +118,7 @@ struct F16Bits {
         return (float)__builtin_bit_cast(_Float16, b);
     }
     __device__ static unsigned short enc(float v) {
-        return __builtin_bit_cast(unsigned short, (_Float16)v);
+        return __builtin_bit_cast(unsigned short, (_Float16)settle(v));
     }
 };
 
@@ -130,6 +142,10 @@ struct Codec16 {
         return __builtin_nontemporal_load(reinterpret_cast<const vec *>(row) + i);
     }
     __device__ static void decode(const vec q, float (&v)[8]) { unpack(q, v); }
+    __device__ static vec encode(const float (&v)[8]) {
+        return vec{B::pack(v[0], v[1]), B::pack(v[2], v[3]),
+                   B::pack(v[4], v[5]), B::pack(v[6], v[7])};
+    }
     __device__ static void load(const T *base, int i, float (&v)[8]) {
         unpack(reinterpret_cast<const vec *>(base)[i], v);
     }
@@ -309,7 +325,7 @@ pass_sumsq(RowArgs p, const void *src, int64_t row0, int chunks, float *part) {
 // inv[rl] = 1/sqrt(sum_c part[rl * chunks + c] / n + eps), one workgroup per
 // row; lane l adds chunks l, l + 256, ... in order, then the lanes' sums are
 // added in a fixed order.
-__global__ void __launch_bounds__(MB)
+[[maybe_unused]] __global__ void __launch_bounds__(MB)
 pass_combine(const float *part, int chunks, int n, float eps, float *inv) {
     __shared__ float red[MB / 64];
     const int64_t rl = blockIdx.x;

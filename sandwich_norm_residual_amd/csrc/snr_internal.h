@@ -15,7 +15,12 @@ enum Op : int {
     OP_NORM_Q8 = 4  // RMSNorm, then Q8_1 records of the normalised row
 };
 enum Storage : int { ST_F32 = 0, ST_BF16 = 1, ST_F16 = 2 };
-enum Kind : int { KIND_ROWTILE = 1, KIND_SPLIT = 2, KIND_MULTIPASS = 3 };
+enum Kind : int {
+    KIND_ROWTILE = 1,
+    KIND_SPLIT = 2,
+    KIND_MULTIPASS = 3,
+    KIND_PERSIST = 4   // persistent row tile: same launcher signature
+};
 
 // Everything a row kernel needs.
 //   OP_PLAIN:    x0 = x, g0 = gamma, out0 = y, eps0
@@ -108,6 +113,7 @@ struct KernelEntry {
 // (snr_kernels.hip), and RMSNorm into Q8_1 records (snr_q8.hip).
 const KernelEntry *kernel_table(int *count);
 const KernelEntry *q8_kernel_table(int *count);
+const KernelEntry *persist_kernel_table(int *count);   // snr_persist.hip
 
 // Zero `words` 32-bit words with a kernel (used instead of a memset so that
 // the call can also be recorded into a HIP graph).

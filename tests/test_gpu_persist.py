@@ -1,0 +1,110 @@
+"""The persistent row tiles (forced shape "persist") against the oracle, and
+bit for bit against the row-tile kernel with the same lanes per row and
+loads per lane (the arithmetic is shared; only the way rows reach the
+registers differs). Large row counts give every workgroup many trips
+through its pipelined loop (odd and even counts)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import sandwich_norm_residual_amd as snr  # noqa: E402
+from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
+from gpu_helpers import (check_add_norm, check_norm_add, check_plain,  # noqa: E402
+                         check_tail, run_add_norm, run_norm_add, run_plain,
+                         run_tail, say)
+
+pytestmark = pytest.mark.gpu
+
+VEC = {"f32": 4, "bf16": 8, "f16": 8}
+SHAPES = [(128, 2), (256, 2), (512, 2), (1024, 1), (1024, 2)]
+OPS = ["plain", "tail", "norm_add", "add_norm"]
+
+
+def _inputs(op, st, rows, n, seed):
+    if op == "plain":
+        return gen.random_plain(rows, n, seed, dtype=st)
+    if op == "tail":
+        return gen.random_tail(rows, n, seed, dtype=st)
+    return gen.random_pair(op, rows, n, seed, dtype=st)
+
+
+def _run(op, inp):
+    if op == "plain":
+        return [run_plain(inp)[0]]
+    if op == "tail":
+        return list(run_tail(inp))
+    if op == "norm_add":
+        return [run_norm_add(inp, scale=1.25)]
+    return list(run_add_norm(inp))
+
+
+def _check(oracle, op, inp, outs, label):
+    if op == "plain":
+        check_plain(oracle, inp, outs[0], label)
+    elif op == "tail":
+        check_tail(oracle, inp, outs[0], outs[1], label)
+    elif op == "norm_add":
+        check_norm_add(oracle, inp, outs[0], 1.25, label)
+    else:
+        check_add_norm(oracle, inp, outs[0], outs[1], label)
+
+
+def _cases():
+    return [(op, st, g, v) for op in OPS for st in ("f32", "bf16", "f16")
+            for g, v in SHAPES]
+
+
+@pytest.mark.parametrize("case", _cases(),
+                         ids=lambda c: "{}-{}-g{}-v{}".format(*c))
+def test_persist_matches_oracle_and_rowtile(oracle, case):
+    op, st, g, v = case
+    w = VEC[st]
+    nv = g * v - g // 2          # a partly filled tile
+    n = nv * w
+    rows = 700
+    label = f"persist-{op}-{st}-g{g}-v{v}-n{n}"
+    say(f"{label} rows={rows}")
+    inp = _inputs(op, st, rows, n, 32000 + g + v + n)
+    with snr.forced_shape("persist", g, v):
+        got = _run(op, inp)
+        assert snr.last_shape() == f"persist:{g}:{v}:{w}", snr.last_shape()
+    _check(oracle, op, inp, got, label)
+    with snr.forced_shape("rowtile", g, v):
+        ref = _run(op, inp)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), label
+
+
+@pytest.mark.parametrize("case", [("tail", "f32", 1024, 2, 4099),
+                                  ("tail", "bf16", 512, 2, 4096),
+                                  ("plain", "f16", 1024, 1, 8195),
+                                  ("add_norm", "bf16", 128, 2, 20001)],
+                         ids=lambda c: "{}-{}-g{}-v{}-rows{}".format(*c))
+def test_persist_many_trips(oracle, case):
+    """Thousands of rows: each workgroup of the resident grid takes several
+    rows in turn. Bit-equal to the row tile; sampled rows against the
+    oracle."""
+    op, st, g, v, rows = case
+    w = VEC[st]
+    n = (g * v - 8) * w
+    label = f"persist-trips-{op}-{st}-g{g}-v{v}-rows{rows}"
+    say(label)
+    inp = _inputs(op, st, rows, n, 33000 + rows)
+    with snr.forced_shape("persist", g, v):
+        got = _run(op, inp)
+    with snr.forced_shape("rowtile", g, v):
+        ref = _run(op, inp)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), label
+    pick = np.r_[0:3, rows // 2:rows // 2 + 3, rows - 3:rows]
+    sub = {k: (val[pick] if isinstance(val, np.ndarray) and val.ndim == 2
+               else val) for k, val in inp.items()}
+    _check(oracle, op, sub, [o[pick] for o in got], label + "-sampled")
+
+
+def test_persist_rejects_ragged_rows():
+    inp = gen.random_plain(4, 4 * 100 + 1, 34000)
+    with snr.forced_shape("persist", 128, 2):
+        with pytest.raises(snr.SnrError):
+            run_plain(inp)
