@@ -1,6 +1,8 @@
 // snr_api.cpp - the C ABI of libsnr (declared in include/snr.h): argument
 // validation, dispatch-shape selection, the split-row workspace and the
-// kernel launches. Host code only; the kernels live in snr_kernels.hip.
+// kernel launches. Host code only; the kernels live in snr_kernels.hip (row
+// tiles, split rows, multi-pass), snr_persist.hip (persistent row tiles) and
+// snr_q8.hip (RMSNorm into Q8_1 records).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
