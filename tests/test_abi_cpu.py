@@ -132,6 +132,10 @@ def test_tail_argument_errors(L):
 
 def test_force_shape_rejects_unknown_kind(L):
     assert L.snr_force_shape(7, 0, 0) == _lib.SNR_ERR_SHAPE
+    for name in ("ROWTILE", "SPLIT", "MULTIPASS", "PERSIST"):
+        code = header_enum(f"SNR_SHAPE_{name}")
+        assert code == getattr(_lib, f"SHAPE_{name}")
+        assert L.snr_force_shape(code, 128, 2) == _lib.SNR_OK
     assert L.snr_force_shape(_lib.SHAPE_AUTO, 0, 0) == _lib.SNR_OK
     buf = ctypes.create_string_buffer(8)
     assert L.snr_last_shape(None, 8) == _lib.SNR_ERR_NULL
