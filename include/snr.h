@@ -8,14 +8,18 @@
  *   memory (row i starts at element i*n); gains are dense [n] vectors shared
  *   by all rows. There is no stride argument.
  * - All pointers are device pointers owned by the caller. The library never
- *   frees or retains them. It owns only a small per-(device, stream) workspace
- *   that the split-row kernels use for cross-workgroup partial sums; it is
- *   allocated on first need and released at process exit.
+ *   frees or retains them. It owns only a per-(device, stream) workspace of
+ *   about 10 MB, for the partial sums of the split-row and multi-pass
+ *   kernels (rows wider than 65536 elements): allocated by the first such
+ *   call on that stream, left zeroed by every launch, kept until the process
+ *   exits. Every other shape allocates nothing.
  * - Calls are asynchronous: they validate the arguments, enqueue kernels on
  *   `stream` (NULL = the legacy default stream of the current device) and
  *   return. Execution faults surface at the caller's next synchronisation.
- *   Arguments are never partially processed: a call that returns an error
- *   code has enqueued nothing.
+ *   Arguments are validated before anything is enqueued: a call that rejects
+ *   its arguments has enqueued nothing. (SNR_ERR_HIP from a failed launch
+ *   can follow earlier launches of the same call, e.g. of other row
+ *   batches.)
  * - Reductions are deterministic: for a given (rows, n, dtype, dispatch
  *   shape) the result is bit-identical from run to run (fixed summation
  *   order, no floating-point atomics).
