@@ -14,8 +14,8 @@
  *   call on that stream, left zeroed by every launch, kept until the process
  *   exits. Every other shape allocates nothing.
  * - Calls are asynchronous: they validate the arguments, enqueue kernels on
- *   `stream` (NULL = the legacy default stream of the current device) and
- *   return. Execution faults surface at the caller's next synchronisation.
+ *   `stream` (NULL = the legacy default stream of the current device; any
+ *   other stream must belong to the current device) and return. Execution faults surface at the caller's next synchronisation.
  *   Arguments are validated before anything is enqueued: a call that rejects
  *   its arguments has enqueued nothing. (SNR_ERR_HIP from a failed launch
  *   can follow earlier launches of the same call, e.g. of other row
@@ -69,7 +69,8 @@ enum {
                               keep every chunk of a row co-resident */
     SNR_ERR_HIP = 8,       /* a HIP runtime call failed; see
                               snr_last_hip_error() */
-    SNR_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+    SNR_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU, or
+                              `stream` belongs to another device */
 };
 
 /*

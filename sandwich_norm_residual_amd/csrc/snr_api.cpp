@@ -52,9 +52,18 @@ struct DeviceInfo {
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
 
-int current_device(int *dev, DeviceInfo *info) {
+// The current device, which must be a gfx950 and own `stream`: the
+// workspace, the occupancy figures and the device check all follow the
+// current device, while HIP runs the kernels on the stream's device.
+int current_device(hipStream_t stream, int *dev, DeviceInfo *info) {
     hipError_t e = hipGetDevice(dev);
     if (e != hipSuccess) return hip_fail(e);
+    if (stream) {
+        hipDevice_t owner = 0;
+        e = hipStreamGetDevice(stream, &owner);
+        if (e != hipSuccess) return hip_fail(e);
+        if (owner != *dev) return SNR_ERR_DEVICE;
+    }
     std::lock_guard<std::mutex> lk(g_dev_mu);
     auto it = g_dev.find(*dev);
     if (it == g_dev.end()) {
@@ -268,7 +277,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
            hipStream_t stream) {
     int dev = 0;
     DeviceInfo info;
-    int rc = current_device(&dev, &info);
+    int rc = current_device(stream, &dev, &info);
     if (rc != SNR_OK) return rc;
 
     // 128-bit vectors need only element alignment on gfx950; the n % w
@@ -603,7 +612,7 @@ int rmsnorm_fwd_multi(const snr_segment *segs, int count, int64_t n,
 
     int dev = 0;
     DeviceInfo info;
-    int rc = current_device(&dev, &info);
+    int rc = current_device(stream, &dev, &info);
     if (rc != SNR_OK) return rc;
     const int w = (int)(16 / es);
     Choice c;
@@ -662,7 +671,9 @@ const char *snr_strerror(int code) {
         return "split-row workspace unavailable or row too wide for "
                "co-resident workgroups";
     case SNR_ERR_HIP: return "HIP runtime call failed";
-    case SNR_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case SNR_ERR_DEVICE:
+        return "current device is not a gfx950 GPU, or the stream belongs to "
+               "another device";
     default: return "unknown error code";
     }
 }
