@@ -60,6 +60,12 @@ def _dtype_code(t) -> int:
 
 
 def _check_tensor(name, t, device, dtype, shape=None):
+    """Raise ValueError unless t is a contiguous tensor on `device` (a GPU)
+    of `dtype` and, when given, `shape`. One combined test on the common
+    path: each tensor attribute read costs about 0.1 us in Python."""
+    if (t.dtype is dtype and t.device == device and t.is_contiguous()
+            and (shape is None or t.shape == shape)):
+        return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.device != device:
@@ -68,9 +74,19 @@ def _check_tensor(name, t, device, dtype, shape=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
-                         f"{tuple(shape)}")
+    raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                     f"{tuple(shape)}")
+
+
+def _lead(name, t):
+    """Check the tensor that fixes a call's device and dtype; return its
+    dtype code."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    code = _dtype_code(t)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return code
 
 
 def _rows_n(t):
@@ -89,18 +105,14 @@ def rmsnorm_fwd(x, gamma, eps: float, out=None):
     computes in place). Runs on the current stream of x's device.
     """
     torch = _torch()
-    _dtype_code(x)
-    _check_tensor("x", x, x.device, x.dtype)
-    rows, n = _rows_n(x)
-    _check_tensor("gamma", gamma, x.device, x.dtype, (n,))
+    rows, n, code = _rows_inputs([("x", x)], [("gamma", gamma)], x)
     if out is None:
         out = torch.empty_like(x)
     else:
-        _check_tensor("out", out, x.device, x.dtype, x.shape)
+        _outputs([("out", out)], x)
     with _on(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
         rc = _lib.rmsnorm_fwd(x.data_ptr(), gamma.data_ptr(), float(eps),
-                              rows, n, _dtype_code(x), out.data_ptr(), stream)
+                              rows, n, code, out.data_ptr(), _stream(x.device))
     _lib.check(rc, "rmsnorm_fwd")
     return out
 
@@ -117,7 +129,7 @@ def rmsnorm_fwd_multi(problems, outs=None):
     if len(problems) > _lib.MAX_SEGMENTS:
         raise ValueError(f"at most {_lib.MAX_SEGMENTS} problems per call")
     x0 = problems[0][0]
-    _dtype_code(x0)
+    code = _lead("x[0]", x0)
     n = x0.shape[-1]
     outs = list(outs) if outs is not None else [None] * len(problems)
     segs = []
@@ -133,27 +145,41 @@ def rmsnorm_fwd_multi(problems, outs=None):
         segs.append((x.data_ptr(), g.data_ptr(), outs[i].data_ptr(), rows,
                      float(eps)))
     with _on(x0.device):
-        rc = _lib.rmsnorm_fwd_multi(segs, n, _dtype_code(x0),
-                                    _stream(x0.device))
+        rc = _lib.rmsnorm_fwd_multi(segs, n, code, _stream(x0.device))
     _lib.check(rc, "rmsnorm_fwd_multi")
     return outs
 
 
 def _stream(dev):
+    """The raw handle of `dev`'s current stream. torch's own C accessor is
+    used where it exists (about 0.2 us against 1.8 us for building the
+    Stream object)."""
     torch = _torch()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and dev.index is not None:
+        return raw(dev.index)
     return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _rows_inputs(names_tensors, gains, like):
-    """Check [..., n] inputs of one dtype/device and [n] gains."""
-    dev, dt = like.device, like.dtype
-    _dtype_code(like)
+    """Check [..., n] inputs of like's dtype, device and shape, and [n]
+    gains. Returns (rows, n, dtype code); `like` itself is checked as the
+    first of names_tensors."""
+    code = _lead(names_tensors[0][0], like)
+    dev, dt, shape = like.device, like.dtype, like.shape
     rows, n = _rows_n(like)
-    for name, t in names_tensors:
-        _check_tensor(name, t, dev, dt, like.shape)
+    for name, t in names_tensors[1:]:
+        _check_tensor(name, t, dev, dt, shape)
     for name, g in gains:
         _check_tensor(name, g, dev, dt, (n,))
-    return rows, n
+    return rows, n, code
+
+
+def _outputs(names_tensors, like):
+    """Check caller-given outputs against like's dtype, device and shape."""
+    dev, dt, shape = like.device, like.dtype, like.shape
+    for name, t in names_tensors:
+        _check_tensor(name, t, dev, dt, shape)
 
 
 def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
@@ -167,14 +193,19 @@ def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
     ``h_out is r`` updates the residual stream in place.
     """
     torch = _torch()
-    rows, n = _rows_inputs([("a", a), ("r", r)],
-                           [("gamma_post", gamma_post),
-                            ("gamma_pre", gamma_pre)], a)
-    h_out = torch.empty_like(a) if h_out is None else h_out
-    y_out = torch.empty_like(a) if y_out is None else y_out
-    _rows_inputs([("h_out", h_out), ("y_out", y_out)], [], a)
+    rows, n, code = _rows_inputs([("a", a), ("r", r)],
+                                 [("gamma_post", gamma_post),
+                                  ("gamma_pre", gamma_pre)], a)
+    if h_out is None:
+        h_out = torch.empty_like(a)
+    else:
+        _outputs([("h_out", h_out)], a)
+    if y_out is None:
+        y_out = torch.empty_like(a)
+    else:
+        _outputs([("y_out", y_out)], a)
     with _on(a.device):
-        if a.dtype == torch.float32:
+        if code == _lib.SNR_F32:
             rc = _lib.sandwich_tail(a.data_ptr(), r.data_ptr(),
                                     gamma_post.data_ptr(), float(eps_post),
                                     gamma_pre.data_ptr(), float(eps_pre),
@@ -184,7 +215,7 @@ def sandwich_tail(a, r, gamma_post, eps_post: float, gamma_pre,
             rc = _lib.sandwich_tail_typed(
                 a.data_ptr(), r.data_ptr(), gamma_post.data_ptr(),
                 float(eps_post), gamma_pre.data_ptr(), float(eps_pre),
-                h_out.data_ptr(), y_out.data_ptr(), rows, n, _dtype_code(a),
+                h_out.data_ptr(), y_out.data_ptr(), rows, n, code,
                 _stream(a.device))
     _lib.check(rc, "sandwich_tail")
     return h_out, y_out
@@ -196,16 +227,18 @@ def sandwich_tail_inplace(a, residual, gamma_post, eps_post: float,
     residual += post-norm(a); returns y, the pre-norm of the updated
     residual."""
     torch = _torch()
-    rows, n = _rows_inputs([("a", a), ("residual", residual)],
-                           [("gamma_post", gamma_post),
-                            ("gamma_pre", gamma_pre)], a)
-    y_out = torch.empty_like(a) if y_out is None else y_out
-    _rows_inputs([("y_out", y_out)], [], a)
+    rows, n, code = _rows_inputs([("a", a), ("residual", residual)],
+                                 [("gamma_post", gamma_post),
+                                  ("gamma_pre", gamma_pre)], a)
+    if y_out is None:
+        y_out = torch.empty_like(a)
+    else:
+        _outputs([("y_out", y_out)], a)
     with _on(a.device):
         rc = _lib.sandwich_tail_inplace(
             a.data_ptr(), residual.data_ptr(), gamma_post.data_ptr(),
             float(eps_post), gamma_pre.data_ptr(), float(eps_pre),
-            y_out.data_ptr(), rows, n, _dtype_code(a), _stream(a.device))
+            y_out.data_ptr(), rows, n, code, _stream(a.device))
     _lib.check(rc, "sandwich_tail_inplace")
     return y_out
 
@@ -216,9 +249,11 @@ def norm_then_add(a, r, gamma, eps: float, out_scale=None, out=None):
     out_scale: None, or a one-element float32 GPU tensor (read on the GPU).
     ``out is r`` updates the residual in place."""
     torch = _torch()
-    rows, n = _rows_inputs([("a", a), ("r", r)], [("gamma", gamma)], a)
-    out = torch.empty_like(a) if out is None else out
-    _rows_inputs([("out", out)], [], a)
+    rows, n, code = _rows_inputs([("a", a), ("r", r)], [("gamma", gamma)], a)
+    if out is None:
+        out = torch.empty_like(a)
+    else:
+        _outputs([("out", out)], a)
     scale_ptr = None
     if out_scale is not None:
         _check_tensor("out_scale", out_scale, a.device, torch.float32)
@@ -228,7 +263,7 @@ def norm_then_add(a, r, gamma, eps: float, out_scale=None, out=None):
     with _on(a.device):
         rc = _lib.norm_then_add(a.data_ptr(), r.data_ptr(), gamma.data_ptr(),
                                 float(eps), scale_ptr, out.data_ptr(), rows,
-                                n, _dtype_code(a), _stream(a.device))
+                                n, code, _stream(a.device))
     _lib.check(rc, "norm_then_add")
     return out
 
@@ -237,14 +272,19 @@ def add_then_norm(a, b, gamma, eps: float, sum_out=None, y_out=None):
     """s = a + b; y = s / sqrt(mean(s^2) + eps) * gamma. Returns (s, y).
     ``sum_out`` may be ``a`` or ``b`` (accumulate in place)."""
     torch = _torch()
-    rows, n = _rows_inputs([("a", a), ("b", b)], [("gamma", gamma)], a)
-    sum_out = torch.empty_like(a) if sum_out is None else sum_out
-    y_out = torch.empty_like(a) if y_out is None else y_out
-    _rows_inputs([("sum_out", sum_out), ("y_out", y_out)], [], a)
+    rows, n, code = _rows_inputs([("a", a), ("b", b)], [("gamma", gamma)], a)
+    if sum_out is None:
+        sum_out = torch.empty_like(a)
+    else:
+        _outputs([("sum_out", sum_out)], a)
+    if y_out is None:
+        y_out = torch.empty_like(a)
+    else:
+        _outputs([("y_out", y_out)], a)
     with _on(a.device):
         rc = _lib.add_then_norm(a.data_ptr(), b.data_ptr(), gamma.data_ptr(),
                                 float(eps), sum_out.data_ptr(),
-                                y_out.data_ptr(), rows, n, _dtype_code(a),
+                                y_out.data_ptr(), rows, n, code,
                                 _stream(a.device))
     _lib.check(rc, "add_then_norm")
     return sum_out, y_out
@@ -259,10 +299,7 @@ def rmsnorm_q8_1(x, gamma, eps: float, out=None):
     multiple of 32; gamma: [n] of the same dtype. Returns (or fills ``out``)
     a uint8 tensor [..., n / 32, 36]."""
     torch = _torch()
-    _dtype_code(x)
-    _check_tensor("x", x, x.device, x.dtype)
-    rows, n = _rows_n(x)
-    _check_tensor("gamma", gamma, x.device, x.dtype, (n,))
+    rows, n, code = _rows_inputs([("x", x)], [("gamma", gamma)], x)
     if n % 32:
         raise ValueError(f"rmsnorm_q8_1 needs n a multiple of 32, got {n}")
     shape = tuple(x.shape[:-1]) + (n // 32, 36)
@@ -272,7 +309,7 @@ def rmsnorm_q8_1(x, gamma, eps: float, out=None):
         _check_tensor("out", out, x.device, torch.uint8, shape)
     with _on(x.device):
         rc = _lib.rmsnorm_q8_1(x.data_ptr(), gamma.data_ptr(), float(eps),
-                               rows, n, _dtype_code(x), out.data_ptr(),
+                               rows, n, code, out.data_ptr(),
                                _stream(x.device))
     _lib.check(rc, "rmsnorm_q8_1")
     return out
