@@ -165,6 +165,25 @@ def make_step(cfg, inp, sets, snr, separate=False):
     return step
 
 
+def capture_steps(step, count: int, torch):
+    """A HIP graph (torch.cuda.CUDAGraph) of `count` consecutive steps,
+    step(0) ... step(count - 1), captured after one eager pass of the same
+    steps on the capture's side stream."""
+    side = torch.cuda.Stream()   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(count):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(count):
+            step(i)
+    torch.cuda.synchronize()
+    return graph
+
+
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
     """The f64 oracle as it stands, rows split across host threads (ctypes
     releases the GIL), repeated over the full workload for about `seconds`."""
@@ -272,6 +291,12 @@ def main() -> int:
     ap.add_argument("--separate-launches", action="store_true",
                     help="several-norm workloads: one rmsnorm_fwd launch per "
                          "problem instead of one rmsnorm_fwd_multi launch")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the steps from HIP graphs (each graph holds "
+                         "one step per buffer set, repeated to 64 or more "
+                         "steps) instead of launching them from Python: the "
+                         "decode-size steps are then bound by the GPU, not "
+                         "by the host's call rate")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run 10 plain device copies of MIB MiB "
                          "(byte-counter calibration under rocprofv3)")
@@ -311,10 +336,21 @@ def main() -> int:
         shape = snr.last_shape()
         torch.cuda.synchronize()
 
+        # `unit` steps per call of run(): one step launched from Python, or
+        # one replay of a graph holding `unit` steps
+        unit = 1
+        run = step
+        if args.graph:
+            unit = len(sets) * max(1, -(-64 // len(sets)))
+            graph = capture_steps(step, unit, torch)
+            run = lambda i: graph.replay()  # noqa: E731
+        calls = max(1, args.steps // unit)
+        steps = calls * unit
+
         # whole-job throughput: K back-to-back steps, synchronised both sides
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i)
+        for i in range(calls):
+            run(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
@@ -323,23 +359,24 @@ def main() -> int:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
-            step(i)
+        for i in range(calls):
+            run(i)
         e1.record(stream)
         torch.cuda.synchronize()
-        mean_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        mean_us = e0.elapsed_time(e1) * 1e3 / steps
 
         # spread of single launches (each bracketed by its own events, which
-        # adds the events' own overhead to every sample)
+        # adds the events' own overhead to every sample; with graphs, the
+        # mean step of each replay)
         ev = [(torch.cuda.Event(enable_timing=True),
                torch.cuda.Event(enable_timing=True))
-              for _ in range(min(args.steps, 200))]
+              for _ in range(max(2, min(calls, 200)))]
         for i in range(len(ev)):
             ev[i][0].record(stream)
-            step(i)
+            run(i)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
-        durs_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        durs_us = [a.elapsed_time(b) * 1e3 / unit for a, b in ev]
 
         if args.copy_probe:
             n = args.copy_probe * (1 << 20) // 4
@@ -350,8 +387,8 @@ def main() -> int:
             torch.cuda.synchronize()
             log(f"copy probe: 10 x {args.copy_probe} MiB device copies")
 
-    ms_per_step = wall / args.steps * 1e3
-    value = nbytes * args.steps / wall / 1e9
+    ms_per_step = wall / steps * 1e3
+    value = nbytes * steps / wall / 1e9
     med_us = statistics.median(durs_us)
     q = statistics.quantiles(durs_us, n=10)
     achieved = nbytes / (mean_us * 1e-6) / 1e9
@@ -371,7 +408,7 @@ def main() -> int:
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
@@ -384,10 +421,11 @@ def main() -> int:
                    "kind": cfg.kind, "eps": list(cfg.eps),
                    "launches_per_step": (len(cfg.segments)
                                          if args.separate_launches else 1),
+                   "steps_per_graph": unit if args.graph else None,
                    "dispatch_shape": shape,
                    "rotating_buffer_sets": len(sets),
                    "algorithmic_bytes_per_step": nbytes},
-        "rows_per_s": round(cfg.rows * args.steps / wall, 1),
+        "rows_per_s": round(cfg.rows * steps / wall, 1),
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "kernel_us": {"mean_over_timed_region": round(mean_us, 3),
                       "single_launch_median": round(med_us, 3),

@@ -69,3 +69,60 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_graph_flag_is_parsed_before_the_gpu_check():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--graph", "--config", "tail_1x6656_f32", "--gpus",
+                        "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_capture_steps_runs_each_step_twice_in_order():
+    """capture_steps: one eager pass on a side stream, then the same steps
+    under capture (torch's graph API replaced by a recorder)."""
+    calls = []
+
+    class _Ctx:
+        def __init__(self, tag):
+            self.tag = tag
+
+        def __enter__(self):
+            calls.append(("enter", self.tag))
+
+        def __exit__(self, *exc):
+            calls.append(("exit", self.tag))
+
+    class _Stream:
+        def wait_stream(self, other):
+            pass
+
+    class _Cuda:
+        Stream = _Stream
+
+        @staticmethod
+        def current_stream():
+            return _Stream()
+
+        @staticmethod
+        def stream(s):
+            return _Ctx("side")
+
+        @staticmethod
+        def synchronize():
+            pass
+
+        class CUDAGraph:
+            pass
+
+        @staticmethod
+        def graph(g):
+            return _Ctx("capture")
+
+    class _Torch:
+        cuda = _Cuda
+
+    g = bench.capture_steps(lambda i: calls.append(i), 3, _Torch)
+    assert isinstance(g, _Cuda.CUDAGraph)
+    assert calls == [("enter", "side"), 0, 1, 2, ("exit", "side"),
+                     ("enter", "capture"), 0, 1, 2, ("exit", "capture")]
