@@ -278,7 +278,9 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=2000,
+                    help="timed steps (the headline's 2000 take about 0.15 s "
+                         "of GPU time per pass)")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=None,
                     help="workload name (default: the 4096x6656 f32 tail)")
