@@ -5,15 +5,22 @@
  * Test infrastructure: tests/test_gpu_c_client.py writes the inputs, runs
  * this program and compares its outputs with the oracle.
  *
- *   snr_client DIR ROWS N
+ *   snr_client DIR ROWS N f32    f32 tail, plain norm and in-place tail
+ *   snr_client DIR ROWS N bf16   every other entry point, bf16 storage
  *
- * reads DIR/a.f32, DIR/r.f32 ([ROWS, N] f32), DIR/gp.f32, DIR/gq.f32 ([N]
- * f32) and DIR/eps.f32 (eps_post, eps_pre), then on a stream of its own:
- *   - sandwich_tail(a, r, gp, eps_post, gq, eps_pre) -> DIR/h.f32, DIR/y.f32
- *   - rmsnorm_fwd(a, gp, eps_pre) in f32 -> DIR/z.f32
- *   - the in-place tail on a copy of r -> DIR/hi.f32 (the updated residual)
- *     and DIR/yi.f32
- * and checks that invalid arguments come back as their error codes with
+ * Inputs (raw little-endian arrays; f32, or bf16 bit patterns): DIR/a, DIR/r
+ * ([ROWS, N]), DIR/gp, DIR/gq ([N]) and DIR/eps (two f32: eps_post,
+ * eps_pre). On a stream of its own it runs, for f32:
+ *   sandwich_tail(a, r, gp, eps_post, gq, eps_pre)      -> DIR/h, DIR/y
+ *   rmsnorm_fwd(a, gp, eps_pre)                          -> DIR/z
+ *   sandwich_tail_inplace on a copy of r                 -> DIR/hi, DIR/yi
+ * and for bf16:
+ *   sandwich_tail_typed(a, r, gp, eps_post, gq, eps_pre) -> DIR/h, DIR/y
+ *   norm_then_add(a, r, gp, eps_post, no scale)          -> DIR/na
+ *   add_then_norm(r, a, gq, eps_pre)                     -> DIR/s, DIR/sy
+ *   rmsnorm_fwd_multi({a, gp}, {r, gq}, eps_pre)         -> DIR/m0, DIR/m1
+ *   rmsnorm_q8_1(a, gp, eps_pre) when N % 32 == 0        -> DIR/q8
+ * after checking that invalid arguments come back as their error codes with
  * nothing enqueued. Prints "ok" and exits 0, or names the failing step and
  * exits 1.
  */
@@ -24,128 +31,181 @@
 
 #include "snr.h"
 
+static const char *g_dir;
+
 static int fail(const char *what, int code) {
     fprintf(stderr, "snr_client: %s failed: %d (%s)\n", what, code,
             code > 0 && code < 100 ? snr_strerror(code) : "hip");
     return 1;
 }
 
-static float *read_file(const char *dir, const char *name, size_t count) {
+/* a device copy of DIR/name (exactly `bytes` long), or NULL */
+static void *upload(const char *name, size_t bytes) {
     char path[4096];
-    snprintf(path, sizeof path, "%s/%s", dir, name);
+    snprintf(path, sizeof path, "%s/%s", g_dir, name);
     FILE *f = fopen(path, "rb");
     if (!f) return NULL;
-    float *buf = (float *)malloc(count * sizeof(float));
-    if (buf && fread(buf, sizeof(float), count, f) != count) {
-        free(buf);
-        buf = NULL;
-    }
+    void *host = malloc(bytes), *dev = NULL;
+    const int ok = host && fread(host, 1, bytes, f) == bytes &&
+                   hipMalloc(&dev, bytes) == hipSuccess &&
+                   hipMemcpy(dev, host, bytes, hipMemcpyHostToDevice) ==
+                       hipSuccess;
     fclose(f);
-    return buf;
+    free(host);
+    return ok ? dev : NULL;
 }
 
-static int write_file(const char *dir, const char *name, const float *buf,
-                      size_t count) {
-    char path[4096];
-    snprintf(path, sizeof path, "%s/%s", dir, name);
-    FILE *f = fopen(path, "wb");
-    if (!f) return 0;
-    const size_t wrote = fwrite(buf, sizeof(float), count, f);
-    fclose(f);
-    return wrote == count;
-}
-
-/* a device copy of a host array */
-static float *upload(const float *host, size_t count) {
+static void *device(size_t bytes) {
     void *d = NULL;
-    if (hipMalloc(&d, count * sizeof(float)) != hipSuccess) return NULL;
-    if (hipMemcpy(d, host, count * sizeof(float), hipMemcpyHostToDevice) !=
-        hipSuccess)
-        return NULL;
-    return (float *)d;
+    return hipMalloc(&d, bytes) == hipSuccess ? d : NULL;
 }
 
-static int download(const char *dir, const char *name, const float *dev,
-                    size_t count) {
-    float *host = (float *)malloc(count * sizeof(float));
-    int ok = host &&
-             hipMemcpy(host, dev, count * sizeof(float),
-                       hipMemcpyDeviceToHost) == hipSuccess &&
-             write_file(dir, name, host, count);
+/* write `bytes` of device memory to DIR/name */
+static int download(const char *name, const void *dev, size_t bytes) {
+    char path[4096];
+    snprintf(path, sizeof path, "%s/%s", g_dir, name);
+    void *host = malloc(bytes);
+    int ok = host != NULL &&
+             hipMemcpy(host, dev, bytes, hipMemcpyDeviceToHost) == hipSuccess;
+    if (ok) {
+        FILE *f = fopen(path, "wb");
+        ok = f != NULL && fwrite(host, 1, bytes, f) == bytes;
+        if (f) fclose(f);
+    }
     free(host);
     return ok;
 }
 
-int main(int argc, char **argv) {
-    if (argc != 4) {
-        fprintf(stderr, "usage: snr_client DIR ROWS N\n");
-        return 2;
-    }
-    const char *dir = argv[1];
-    const int64_t rows = strtoll(argv[2], NULL, 10);
-    const int64_t n = strtoll(argv[3], NULL, 10);
-    if (rows < 1 || n < 1) return fail("arguments", 0);
-    const size_t tn = (size_t)rows * (size_t)n;
-
-    float *a = read_file(dir, "a.f32", tn), *r = read_file(dir, "r.f32", tn);
-    float *gp = read_file(dir, "gp.f32", (size_t)n);
-    float *gq = read_file(dir, "gq.f32", (size_t)n);
-    float *eps = read_file(dir, "eps.f32", 2);
-    if (!a || !r || !gp || !gq || !eps) return fail("reading inputs", 0);
-
-    hipStream_t stream = NULL;
-    if (hipStreamCreate(&stream) != hipSuccess)
-        return fail("hipStreamCreate", 0);
-    float *da = upload(a, tn), *dr = upload(r, tn), *dri = upload(r, tn);
-    float *dgp = upload(gp, (size_t)n), *dgq = upload(gq, (size_t)n);
-    float *dh = NULL, *dy = NULL, *dz = NULL, *dyi = NULL;
-    if (!da || !dr || !dri || !dgp || !dgq ||
-        hipMalloc((void **)&dh, tn * sizeof(float)) != hipSuccess ||
-        hipMalloc((void **)&dy, tn * sizeof(float)) != hipSuccess ||
-        hipMalloc((void **)&dz, tn * sizeof(float)) != hipSuccess ||
-        hipMalloc((void **)&dyi, tn * sizeof(float)) != hipSuccess)
-        return fail("device allocation", 0);
+static int run_f32(int64_t rows, int64_t n, const float *eps,
+                   hipStream_t stream) {
+    const size_t tb = (size_t)rows * (size_t)n * 4, gb = (size_t)n * 4;
+    float *a = upload("a", tb), *r = upload("r", tb), *ri = upload("r", tb);
+    float *gp = upload("gp", gb), *gq = upload("gq", gb);
+    float *h = device(tb), *y = device(tb), *z = device(tb), *yi = device(tb);
+    if (!a || !r || !ri || !gp || !gq || !h || !y || !z || !yi)
+        return fail("inputs or device allocation", 0);
 
     /* invalid arguments: each is refused before anything is enqueued */
-    int rc = sandwich_tail(NULL, dr, dgp, eps[0], dgq, eps[1], dh, dy, rows,
-                           n, stream);
+    int rc = sandwich_tail(NULL, r, gp, eps[0], gq, eps[1], h, y, rows, n,
+                           stream);
     if (rc != SNR_ERR_NULL) return fail("NULL input check", rc);
-    rc = sandwich_tail(da, dr, dgp, 0.0f, dgq, eps[1], dh, dy, rows, n,
-                       stream);
+    rc = sandwich_tail(a, r, gp, 0.0f, gq, eps[1], h, y, rows, n, stream);
     if (rc != SNR_ERR_EPS) return fail("eps check", rc);
-    rc = sandwich_tail(da, dr, dgp, eps[0], dgq, eps[1], dh, da, rows, n,
-                       stream);
+    rc = sandwich_tail(a, r, gp, eps[0], gq, eps[1], h, a, rows, n, stream);
     if (rc != SNR_ERR_ALIAS) return fail("alias check", rc);
-    rc = rmsnorm_fwd(da, dgp, eps[1], rows, n, 7, dz, stream);
+    rc = rmsnorm_fwd(a, gp, eps[1], rows, n, 7, z, stream);
     if (rc != SNR_ERR_DTYPE) return fail("dtype check", rc);
-    rc = rmsnorm_fwd(da, dgp, eps[1], rows, 0, SNR_F32, dz, stream);
+    rc = rmsnorm_fwd(a, gp, eps[1], rows, 0, SNR_F32, z, stream);
     if (rc != SNR_ERR_SHAPE) return fail("shape check", rc);
-    rc = rmsnorm_fwd(da, dgp, eps[1], 0, n, SNR_F32, dz, stream);
+    rc = rmsnorm_fwd(a, gp, eps[1], 0, n, SNR_F32, z, stream);
     if (rc != SNR_OK) return fail("rows == 0 no-op", rc);
 
-    rc = sandwich_tail(da, dr, dgp, eps[0], dgq, eps[1], dh, dy, rows, n,
-                       stream);
+    rc = sandwich_tail(a, r, gp, eps[0], gq, eps[1], h, y, rows, n, stream);
     if (rc != SNR_OK) return fail("sandwich_tail", rc);
-    rc = rmsnorm_fwd(da, dgp, eps[1], rows, n, SNR_F32, dz, stream);
+    rc = rmsnorm_fwd(a, gp, eps[1], rows, n, SNR_F32, z, stream);
     if (rc != SNR_OK) return fail("rmsnorm_fwd", rc);
-    rc = sandwich_tail_inplace(da, dri, dgp, eps[0], dgq, eps[1], dyi, rows,
-                               n, SNR_F32, stream);
+    rc = sandwich_tail_inplace(a, ri, gp, eps[0], gq, eps[1], yi, rows, n,
+                               SNR_F32, stream);
     if (rc != SNR_OK) return fail("sandwich_tail_inplace", rc);
     if (hipStreamSynchronize(stream) != hipSuccess)
         return fail("hipStreamSynchronize", 0);
+    if (!download("h", h, tb) || !download("y", y, tb) ||
+        !download("z", z, tb) || !download("hi", ri, tb) ||
+        !download("yi", yi, tb))
+        return fail("writing outputs", 0);
+    void *all[] = {a, r, ri, gp, gq, h, y, z, yi};
+    for (size_t i = 0; i < sizeof all / sizeof all[0]; ++i)
+        (void)hipFree(all[i]);
+    return 0;
+}
+
+static int run_bf16(int64_t rows, int64_t n, const float *eps,
+                    hipStream_t stream) {
+    const size_t tb = (size_t)rows * (size_t)n * 2, gb = (size_t)n * 2;
+    const size_t qb = (size_t)rows * (size_t)(n / 32) * 36;
+    void *a = upload("a", tb), *r = upload("r", tb);
+    void *gp = upload("gp", gb), *gq = upload("gq", gb);
+    void *h = device(tb), *y = device(tb), *na = device(tb), *s = device(tb);
+    void *sy = device(tb), *m0 = device(tb), *m1 = device(tb);
+    void *q8 = n % 32 == 0 ? device(qb) : NULL;
+    if (!a || !r || !gp || !gq || !h || !y || !na || !s || !sy || !m0 ||
+        !m1 || (n % 32 == 0 && !q8))
+        return fail("inputs or device allocation", 0);
+
+    int rc = sandwich_tail_typed(a, r, gp, eps[0], gq, eps[1], h, y, rows, n,
+                                 3, stream);
+    if (rc != SNR_ERR_DTYPE) return fail("dtype check", rc);
+    rc = norm_then_add(a, r, gp, eps[0], NULL, a, rows, n, SNR_BF16, stream);
+    if (rc != SNR_ERR_ALIAS) return fail("norm_then_add alias check", rc);
+    rc = add_then_norm(r, a, gq, -1.0f, s, sy, rows, n, SNR_BF16, stream);
+    if (rc != SNR_ERR_EPS) return fail("add_then_norm eps check", rc);
+    if (n % 32 != 0) {
+        rc = rmsnorm_q8_1(a, gp, eps[1], rows, n, SNR_BF16, s, stream);
+        if (rc != SNR_ERR_SHAPE) return fail("q8 width check", rc);
+    }
+    snr_segment bad[1] = {{a, gp, a, rows, eps[1]}};
+    bad[0].y = (char *)a + 2; /* overlaps x without coinciding */
+    rc = rmsnorm_fwd_multi(bad, 1, n, SNR_BF16, stream);
+    if (rc != SNR_ERR_ALIAS) return fail("multi alias check", rc);
+
+    rc = sandwich_tail_typed(a, r, gp, eps[0], gq, eps[1], h, y, rows, n,
+                             SNR_BF16, stream);
+    if (rc != SNR_OK) return fail("sandwich_tail_typed", rc);
+    rc = norm_then_add(a, r, gp, eps[0], NULL, na, rows, n, SNR_BF16,
+                       stream);
+    if (rc != SNR_OK) return fail("norm_then_add", rc);
+    rc = add_then_norm(r, a, gq, eps[1], s, sy, rows, n, SNR_BF16, stream);
+    if (rc != SNR_OK) return fail("add_then_norm", rc);
+    snr_segment segs[2] = {{a, gp, m0, rows, eps[1]}, {r, gq, m1, rows, eps[1]}};
+    rc = rmsnorm_fwd_multi(segs, 2, n, SNR_BF16, stream);
+    if (rc != SNR_OK) return fail("rmsnorm_fwd_multi", rc);
+    if (q8) {
+        rc = rmsnorm_q8_1(a, gp, eps[1], rows, n, SNR_BF16, q8, stream);
+        if (rc != SNR_OK) return fail("rmsnorm_q8_1", rc);
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return fail("hipStreamSynchronize", 0);
+    if (!download("h", h, tb) || !download("y", y, tb) ||
+        !download("na", na, tb) || !download("s", s, tb) ||
+        !download("sy", sy, tb) || !download("m0", m0, tb) ||
+        !download("m1", m1, tb) || (q8 && !download("q8", q8, qb)))
+        return fail("writing outputs", 0);
+    void *all[] = {a, r, gp, gq, h, y, na, s, sy, m0, m1, q8};
+    for (size_t i = 0; i < sizeof all / sizeof all[0]; ++i)
+        if (all[i]) (void)hipFree(all[i]);
+    return 0;
+}
+
+int main(int argc, char **argv) {
+    if (argc != 5) {
+        fprintf(stderr, "usage: snr_client DIR ROWS N f32|bf16\n");
+        return 2;
+    }
+    g_dir = argv[1];
+    const int64_t rows = strtoll(argv[2], NULL, 10);
+    const int64_t n = strtoll(argv[3], NULL, 10);
+    const int bf16 = strcmp(argv[4], "bf16") == 0;
+    if (rows < 1 || n < 1 || (!bf16 && strcmp(argv[4], "f32") != 0))
+        return fail("arguments", 0);
+
+    float eps[2];
+    {
+        char path[4096];
+        snprintf(path, sizeof path, "%s/eps", g_dir);
+        FILE *f = fopen(path, "rb");
+        const int ok = f && fread(eps, sizeof(float), 2, f) == 2;
+        if (f) fclose(f);
+        if (!ok) return fail("reading eps", 0);
+    }
+    hipStream_t stream = NULL;
+    if (hipStreamCreate(&stream) != hipSuccess)
+        return fail("hipStreamCreate", 0);
+    const int rc = bf16 ? run_bf16(rows, n, eps, stream)
+                        : run_f32(rows, n, eps, stream);
+    if (rc != 0) return rc;
     if (snr_last_hip_error() != 0)
         return fail("snr_last_hip_error", snr_last_hip_error());
-
-    if (!download(dir, "h.f32", dh, tn) || !download(dir, "y.f32", dy, tn) ||
-        !download(dir, "z.f32", dz, tn) || !download(dir, "hi.f32", dri, tn) ||
-        !download(dir, "yi.f32", dyi, tn))
-        return fail("writing outputs", 0);
-
-    (void)hipFree(da); (void)hipFree(dr); (void)hipFree(dri);
-    (void)hipFree(dgp); (void)hipFree(dgq); (void)hipFree(dh);
-    (void)hipFree(dy); (void)hipFree(dz); (void)hipFree(dyi);
     (void)hipStreamDestroy(stream);
-    free(a); free(r); free(gp); free(gq); free(eps);
     printf("ok\n");
     return 0;
 }

@@ -1,9 +1,9 @@
 """The C ABI called from a plain C program (tests/c_client/snr_client.c,
 built by __graft_entry__.build() with gcc): nothing but libsnr and the HIP
 runtime in the calling process, no PyTorch. Inputs come from the seeded
-generator, and outputs are compared with the oracle here, so the program
-checks the boundary as a C caller meets it: f32 tail, plain norm, in-place
-tail, error codes of rejected calls, and a stream of the caller's own."""
+generator and outputs are compared with the oracle here, so the program
+checks the boundary as a C caller meets it: every entry point, the error
+codes of rejected calls, and a stream of the caller's own."""
 import os
 import subprocess
 
@@ -11,39 +11,44 @@ import numpy as np
 import pytest
 
 from sandwich_norm_residual_amd import inputs as gen
+from gpu_helpers import check_add_norm, check_norm_add, check_plain, \
+    check_q8, check_tail
 from parity import TOL_F32, plain_error, tail_errors
 
 CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_client",
                       "snr_client")
+pytestmark = pytest.mark.gpu
 
 
-def _write(path, arr):
-    np.ascontiguousarray(arr, dtype=np.float32).tofile(path)
-
-
-def _read(path, rows, n):
-    return np.fromfile(path, dtype=np.float32).reshape(rows, n)
-
-
-@pytest.mark.gpu
-@pytest.mark.parametrize("rows,n", [(3, 6657), (64, 6656), (5, 2),
-                                    (2, 65536 + 3)])
-def test_c_client_matches_the_oracle(oracle, tmp_path, rows, n):
+def _run(tmp_path, inp, rows, n, mode):
     assert os.path.exists(CLIENT), (
         f"{CLIENT} is not built; run __graft_entry__.build()")
-    inp = gen.random_tail(rows, n, seed=9100 + n % 97 + rows)
     for key, name in (("a", "a"), ("r", "r"), ("gamma_post", "gp"),
                       ("gamma_pre", "gq")):
-        _write(tmp_path / f"{name}.f32", inp[key])
-    _write(tmp_path / "eps.f32", [inp["eps_post"], inp["eps_pre"]])
-    print(f"[gpu-case] C client rows={rows} n={n}", flush=True)
-    run = subprocess.run([CLIENT, str(tmp_path), str(rows), str(n)],
+        np.ascontiguousarray(inp[key]).tofile(tmp_path / name)
+    np.array([inp["eps_post"], inp["eps_pre"]], np.float32).tofile(
+        tmp_path / "eps")
+    print(f"[gpu-case] C client {mode} rows={rows} n={n}", flush=True)
+    run = subprocess.run([CLIENT, str(tmp_path), str(rows), str(n), mode],
                          capture_output=True, text=True, timeout=90)
     assert run.returncode == 0 and run.stdout.strip() == "ok", (
         run.returncode, run.stdout, run.stderr)
 
-    h = _read(tmp_path / "h.f32", rows, n)
-    y = _read(tmp_path / "y.f32", rows, n)
+
+def _read(path, rows, n, mode):
+    if mode == "f32":
+        return np.fromfile(path, dtype=np.float32).reshape(rows, n)
+    bits = np.fromfile(path, dtype=np.uint16).reshape(rows, n)
+    return gen.from_storage(bits, "bf16").astype(np.float64)
+
+
+@pytest.mark.parametrize("rows,n", [(3, 6657), (64, 6656), (5, 2),
+                                    (2, 65536 + 3)])
+def test_f32_entry_points(oracle, tmp_path, rows, n):
+    inp = gen.random_tail(rows, n, seed=9100 + n % 97 + rows)
+    _run(tmp_path, inp, rows, n, "f32")
+    h = _read(tmp_path / "h", rows, n, "f32")
+    y = _read(tmp_path / "y", rows, n, "f32")
     o = oracle.sandwich_tail(inp["a"], inp["r"], inp["gamma_post"],
                              inp["eps_post"], inp["gamma_pre"], inp["eps_pre"])
     eh, ey = tail_errors(h, y, o, inp["r"], inp["gamma_pre"])
@@ -51,13 +56,39 @@ def test_c_client_matches_the_oracle(oracle, tmp_path, rows, n):
           flush=True)
     assert eh <= TOL_F32 and ey <= TOL_F32, (eh, ey)
 
-    z = _read(tmp_path / "z.f32", rows, n)
+    z = _read(tmp_path / "z", rows, n, "f32")
     want = oracle.rmsnorm(inp["a"], inp["gamma_post"], inp["eps_pre"])
-    ez = plain_error(z, want)
-    assert ez <= TOL_F32, ez
+    assert plain_error(z, want) <= TOL_F32
 
     # the in-place form runs the same kernel on the same shape
-    hi = _read(tmp_path / "hi.f32", rows, n)
-    yi = _read(tmp_path / "yi.f32", rows, n)
+    hi = _read(tmp_path / "hi", rows, n, "f32")
+    yi = _read(tmp_path / "yi", rows, n, "f32")
     assert np.array_equal(hi.view(np.uint32), h.view(np.uint32))
     assert np.array_equal(yi.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,n", [(4, 6656), (3, 100), (2, 65536 + 8)])
+def test_bf16_entry_points(oracle, tmp_path, rows, n):
+    inp = gen.random_tail(rows, n, seed=9300 + n % 89 + rows, dtype="bf16")
+    _run(tmp_path, inp, rows, n, "bf16")
+    rd = lambda name: _read(tmp_path / name, rows, n, "bf16")  # noqa: E731
+    base = {"dtype": "bf16"}
+    check_tail(oracle, inp, rd("h"), rd("y"), "C client bf16 tail")
+    check_norm_add(oracle, {**base, "a": inp["a"], "b": inp["r"],
+                            "gamma": inp["gamma_post"],
+                            "eps": inp["eps_post"]},
+                   rd("na"), None, "C client norm_then_add")
+    check_add_norm(oracle, {**base, "a": inp["r"], "b": inp["a"],
+                            "gamma": inp["gamma_pre"], "eps": inp["eps_pre"]},
+                   rd("s"), rd("sy"), "C client add_then_norm")
+    check_plain(oracle, {**base, "x": inp["a"], "gamma": inp["gamma_post"],
+                         "eps": inp["eps_pre"]}, rd("m0"),
+                "C client multi segment 0")
+    check_plain(oracle, {**base, "x": inp["r"], "gamma": inp["gamma_pre"],
+                         "eps": inp["eps_pre"]}, rd("m1"),
+                "C client multi segment 1")
+    if n % 32 == 0:
+        rec = np.fromfile(tmp_path / "q8", dtype=np.uint8).reshape(
+            rows, n // 32, 36)
+        check_q8(oracle, {**base, "x": inp["a"], "gamma": inp["gamma_post"],
+                          "eps": inp["eps_pre"]}, rec, "C client Q8_1")
