@@ -41,6 +41,8 @@ def log(msg: str) -> None:
 # row streams (reads + writes) and gains of each operation
 STREAMS = {"plain": (2, 1), "tail": (4, 2), "norm_add": (3, 1),
            "add_norm": (4, 1), "multi": (2, 1)}
+# row streams read, of those
+READS = {"plain": 1, "tail": 2, "norm_add": 2, "add_norm": 2, "multi": 1}
 
 
 def algorithmic_bytes(cfg) -> int:
@@ -52,6 +54,104 @@ def algorithmic_bytes(cfg) -> int:
     if cfg.kind == "multi":
         gains = len(cfg.segments)
     return streams * cfg.rows * cfg.n * es + gains * cfg.n * es
+
+
+def read_write_bytes(cfg):
+    """(bytes read, bytes written) of one step; gains count as reads."""
+    es = 4 if cfg.dtype == "f32" else 2
+    total = algorithmic_bytes(cfg)
+    if cfg.kind == "q8":
+        written = cfg.rows * cfg.n // 32 * 36
+    else:
+        written = (STREAMS[cfg.kind][0] - READS[cfg.kind]) * cfg.rows * \
+            cfg.n * es
+    return total - written, written
+
+
+# the streaming kernels of bench_stream.hip, by variant index
+PROBE_READ, PROBE_WRITE, PROBE_WRITE_NT, PROBE_COPY = 0, 1, 2, 3
+PROBE_MIB = 256          # per stream and buffer set
+PROBE_GRIDS = (2048, 8192, 32768, 0)   # 0: one workgroup per trip's range
+
+
+def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
+    """What plain streaming kernels (no arithmetic) sustain on this GPU, and
+    the floor that sets for this workload's step.
+
+    Reads alone and writes alone each stream faster than any mix of the two:
+    an HBM channel turns its bus around between reads and writes. So the
+    floor is a plain copy of the step's W written bytes (W bytes read, W
+    written, in one launch) plus the step's remaining R - W read bytes at
+    the read-only rate (R >= W for every workload here). The copy runs over
+    rotating buffer sets of at least 1 GiB together, like the step; the
+    read-only and write-only rates use 256 MiB buffers. Each figure is the
+    best over a few grid sizes of a flat grid-stride loop, timed by one
+    event pair around 30 back-to-back launches."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_stream.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.stream_probe.restype = ctypes.c_int
+    lib.stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_void_p]
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda:0")
+    handle = stream.cuda_stream
+
+    def buffers(nbytes):
+        nsets = min(64, max(3, -(-(1 << 30) // (2 * nbytes))))
+        return [(torch.ones(nbytes // 4, device="cuda:0"),
+                 torch.empty(nbytes // 4, device="cuda:0"))
+                for _ in range(nsets)]
+
+    def best_us(variant, bufs, nbytes):
+        def launch(i):
+            src, dst = bufs[i % len(bufs)]
+            rc = lib.stream_probe(variant, src.data_ptr(), dst.data_ptr(),
+                                  sink.data_ptr(), nbytes, grid, handle)
+            if rc != 0:
+                raise RuntimeError(f"stream_probe({variant}, {grid}) -> {rc}")
+        best = float("inf")
+        for grid in PROBE_GRIDS:
+            with torch.cuda.stream(stream):
+                for i in range(5):
+                    launch(i)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(30):
+                    launch(i)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / 30)
+        return best
+
+    big = PROBE_MIB << 20
+    bufs = buffers(big)
+    rd = big / best_us(PROBE_READ, bufs, big) * 1e-3
+    wr = big / min(best_us(PROBE_WRITE, bufs, big),
+                   best_us(PROBE_WRITE_NT, bufs, big)) * 1e-3
+    del bufs
+    r_bytes, w_bytes = read_write_bytes(cfg)
+    w16 = w_bytes // 16 * 16
+    copy_us = best_us(PROBE_COPY, buffers(w16), w16)
+    floor_us = copy_us + (r_bytes - w_bytes) / rd * 1e-3
+    floor_gbs = (r_bytes + w_bytes) / (floor_us * 1e-6) / 1e9
+    return {"read_gbs": round(rd, 1), "write_gbs": round(wr, 1),
+            "copy_gbs": round(2 * w16 / copy_us * 1e-3, 1),
+            "copy_us": round(copy_us, 3),
+            "step_read_bytes": r_bytes, "step_write_bytes": w_bytes,
+            "floor_us": round(floor_us, 3), "floor_gbs": round(floor_gbs, 1),
+            "floor_frac_of_peak": round(floor_gbs / PEAK_HBM_GBS, 4),
+            "achieved_frac_of_floor": round(achieved_gbs / floor_gbs, 4),
+            "model": "copy of W bytes in one launch + (R - W) / read_gbs",
+            "probe": (f"plain read / write / copy kernels "
+                      f"(bench_stream.hip); copy of the step's written "
+                      f"bytes over rotating sets of >= 1 GiB; read and "
+                      f"write over {PROBE_MIB} MiB buffers; best of grids "
+                      f"{list(PROBE_GRIDS)} (0 = one trip)")}
 
 
 def kernel_sources(cfg) -> list:
@@ -299,6 +399,9 @@ def main() -> int:
                          "steps) instead of launching them from Python: the "
                          "decode-size steps are then bound by the GPU, not "
                          "by the host's call rate")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-rate kernels that state the "
+                         "attainable HBM floor of the workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run 10 plain device copies of MIB MiB "
                          "(byte-counter calibration under rocprofv3)")
@@ -399,6 +502,17 @@ def main() -> int:
         f"median {med_us:.2f} p10 {q[0]:.2f} p90 {q[-1]:.2f}")
     traffic = measured_traffic(cfg, shape)
 
+    # the floor needs an HBM-bound step: at least 64 MiB of traffic
+    ceiling = None
+    if not args.no_ceiling and nbytes >= (64 << 20):
+        ceiling = stream_ceiling(cfg, torch, stream, achieved)
+        log(f"attainable: read {ceiling['read_gbs']} GB/s, write "
+            f"{ceiling['write_gbs']} GB/s, copy of the step's written bytes "
+            f"{ceiling['copy_us']} us = {ceiling['copy_gbs']} GB/s; "
+            f"floor {ceiling['floor_us']} us/step = "
+            f"{100 * ceiling['floor_frac_of_peak']:.1f}% of peak; this step "
+            f"reaches {100 * ceiling['achieved_frac_of_floor']:.1f}% of it")
+
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
@@ -437,6 +551,7 @@ def main() -> int:
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
+        "attainable": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

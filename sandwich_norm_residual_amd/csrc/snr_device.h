@@ -47,6 +47,9 @@ struct Codec<ST_F32> {
             reinterpret_cast<const vec *>(row) + i);
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
+    __device__ static vec load_raw(const T *base, int i) {
+        return reinterpret_cast<const vec *>(base)[i];
+    }
     __device__ static void load(const T *base, int i, float (&v)[4]) {
         const vec q = reinterpret_cast<const vec *>(base)[i];
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -145,6 +148,9 @@ struct Codec16 {
     __device__ static vec encode(const float (&v)[8]) {
         return vec{B::pack(v[0], v[1]), B::pack(v[2], v[3]),
                    B::pack(v[4], v[5]), B::pack(v[6], v[7])};
+    }
+    __device__ static vec load_raw(const T *base, int i) {
+        return reinterpret_cast<const vec *>(base)[i];
     }
     __device__ static void load(const T *base, int i, float (&v)[8]) {
         unpack(reinterpret_cast<const vec *>(base)[i], v);

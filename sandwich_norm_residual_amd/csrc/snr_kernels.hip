@@ -104,6 +104,49 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                                               : 0.0f;
         }
     }
+    // Gains are loaded one vector just before its use, except that
+    // norm_then_add loads its gain with the row (PRE) where registers allow:
+    // measured 53.5 -> 52.6 us at 4096 x 6656 f32. The vector memory counter
+    // retires in issue order and counts stores too, so a gain loaded between
+    // two stores is waited for together with the first store; the tail, the
+    // plain norm and add_then_norm measured no faster without those waits
+    // (the tail 71.4 -> 74.7 us with its gains loaded with the row), so they
+    // keep the late loads.
+    using V = typename C::vec;
+    constexpr bool PRE = OP == OP_NORM_ADD && !LATE && VPT <= 4;
+    constexpr int NG = OP == OP_TAIL ? 2 : 1;
+    const T *gp[2] = {static_cast<const T *>(p.g0),
+                      static_cast<const T *>(OP == OP_TAIL ? p.g1 : p.g0)};
+    V gq[NG][PRE ? VPT : 1];   // as stored, decoded where used
+    float ge[NG][PRE ? EX : 1];
+    (void)gq;
+    (void)ge;
+    if constexpr (PRE) {
+#pragma unroll
+        for (int w = 0; w < NG; ++w) {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int i = vbase + k * vstride;
+                gq[w][k] = (live && i < nv) ? C::load_raw(gp[w], i) : V{};
+            }
+#pragma unroll
+            for (int q = 0; q < EX; ++q) {
+                const int j = sbase + q * sstride;
+                ge[w][q] = (live && sown && j < rem) ? C::load1(gp[w], tail0 + j)
+                                                     : 0.0f;
+            }
+        }
+    }
+    // gain w's values at vector slot k (index i) and remainder slot q (j)
+    auto gain = [&](int w, int k, int i, float(&g)[W]) {
+        if constexpr (PRE) C::decode(gq[w][k], g);
+        else C::load(gp[w], i, g);
+    };
+    auto gain1 = [&](int w, int q, int j) {
+        if constexpr (PRE) return ge[w][q];
+        else return C::load1(gp[w], tail0 + j);
+    };
+
     T *out0 = static_cast<T *>(p.out0) + off;
     if constexpr (OP == OP_ADD_NORM) {
         // s = a + b, rounded to storage, stored, and kept for the norm.
@@ -134,7 +177,6 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
 #pragma unroll
     for (int q = 0; q < EX; ++q) s = fmaf(e0[q], e0[q], s);
     const float inv0 = inv_rms(reduce(s, 0), p.n, p.eps0);
-    const T *g0 = static_cast<const T *>(p.g0);
 
     if constexpr (OP == OP_PLAIN || OP == OP_ADD_NORM) {
         // y = x * inv * gamma (add_then_norm: x is the stored sum)
@@ -144,7 +186,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             const int i = vbase + k * vstride;
             if (live && i < nv) {
                 float g[W], o[W];
-                C::load(g0, i, g);
+                gain(0, k, i, g);
 #pragma unroll
                 for (int e = 0; e < W; ++e) o[e] = v0[k][e] * inv0 * g[e];
                 C::store_nt(y, i, o);
@@ -154,8 +196,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
         for (int q = 0; q < EX; ++q) {
             const int j = sbase + q * sstride;
             if (live && sown && j < rem)
-                C::store1_nt(y, tail0 + j,
-                             e0[q] * inv0 * C::load1(g0, tail0 + j));
+                C::store1_nt(y, tail0 + j, e0[q] * inv0 * gain1(0, q, j));
         }
     } else {
         // h = r + a * inv * gamma0, kept in registers (v1/e1, or v0/e0 once
@@ -168,7 +209,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             const int i = vbase + k * vstride;
             if (live && i < nv) {
                 float g[W], rr[W];
-                C::load(g0, i, g);
+                gain(0, k, i, g);
                 if constexpr (LATE) {
                     C::load_nt(x1, i, rr);
                 } else {
@@ -194,8 +235,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             const int j = sbase + q * sstride;
             if (live && sown && j < rem) {
                 const float rr = LATE ? C::load1_nt(x1, tail0 + j) : e1[q];
-                const float h =
-                    fmaf(e0[q] * inv0, C::load1(g0, tail0 + j), rr);
+                const float h = fmaf(e0[q] * inv0, gain1(0, q, j), rr);
                 if constexpr (OP == OP_TAIL) {
                     he[q] = C::round(h);
                     C::store1_nt(out0, tail0 + j, he[q]);
@@ -212,14 +252,13 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             for (int q = 0; q < EX; ++q) sh = fmaf(he[q], he[q], sh);
             const float inv1 = inv_rms(reduce(sh, 1), p.n, p.eps1);
 
-            const T *g1 = static_cast<const T *>(p.g1);
             T *out1 = static_cast<T *>(p.out1) + off;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int i = vbase + k * vstride;
                 if (live && i < nv) {
                     float g[W], o[W];
-                    C::load(g1, i, g);
+                    gain(1, k, i, g);
 #pragma unroll
                     for (int e = 0; e < W; ++e) o[e] = hv[k][e] * inv1 * g[e];
                     C::store_nt(out1, i, o);
@@ -229,8 +268,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
             for (int q = 0; q < EX; ++q) {
                 const int j = sbase + q * sstride;
                 if (live && sown && j < rem)
-                    C::store1_nt(out1, tail0 + j,
-                                 he[q] * inv1 * C::load1(g1, tail0 + j));
+                    C::store1_nt(out1, tail0 + j, he[q] * inv1 * gain1(1, q, j));
             }
         }
     }

@@ -126,3 +126,41 @@ def test_capture_steps_runs_each_step_twice_in_order():
     assert isinstance(g, _Cuda.CUDAGraph)
     assert calls == [("enter", "side"), 0, 1, 2, ("exit", "side"),
                      ("enter", "capture"), 0, 1, 2, ("exit", "capture")]
+
+
+def test_read_write_split():
+    cfgs = gen.CONFIGS
+    # tail: a and r and both gains read; h and y written
+    assert bench.read_write_bytes(cfgs["tail_4096x6656_f32"]) == \
+        (8 * 4096 * 6656 + 2 * 4 * 6656, 8 * 4096 * 6656)
+    # plain bf16: x and the gain read, y written
+    assert bench.read_write_bytes(cfgs["plain_16384x4096_bf16"]) == \
+        (2 * 16384 * 4096 + 2 * 4096, 2 * 16384 * 4096)
+    # Q8_1: x and the gain read, records written
+    assert bench.read_write_bytes(cfgs["q8_4096x6656_f32"]) == \
+        (4 * 4096 * 6656 + 4 * 6656, 4096 * 6656 // 32 * 36)
+    for name, cfg in cfgs.items():
+        r, w = bench.read_write_bytes(cfg)
+        assert r >= w > 0 and r + w == bench.algorithmic_bytes(cfg), name
+
+
+def test_stream_probe_library_exports():
+    """bench_stream.so (built by build()) loads without a GPU and exports its
+    two entry points; the argument checks run before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_stream.so")
+    if not os.path.exists(path):
+        pytest.skip("bench_stream.so not built")
+    lib = ctypes.CDLL(path)
+    assert lib.stream_probe_variants() == 4
+    lib.stream_probe.restype = ctypes.c_int
+    lib.stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_void_p]
+    # invalid variant, size not a multiple of 16, null or misaligned buffers
+    assert lib.stream_probe(4, 16, 16, 16, 16, 0, None) == -1
+    assert lib.stream_probe(0, 16, 16, 16, 24, 0, None) == -1
+    assert lib.stream_probe(0, None, 16, 16, 16, 0, None) == -1
+    assert lib.stream_probe(3, 16, 8, 16, 16, 0, None) == -1
+    assert lib.stream_probe(0, 16, None, None, 16, 0, None) == -1
