@@ -88,6 +88,8 @@ def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
     best over a few grid sizes of a flat grid-stride loop, timed by one
     event pair around 30 back-to-back launches."""
     import ctypes
+    # loaded after torch has initialised its own HIP runtime (the library
+    # names the same runtime soname; a process keeps the first copy loaded)
     path = os.path.join(ROOT, "bench_stream.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")

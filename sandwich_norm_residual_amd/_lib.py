@@ -89,6 +89,11 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIBRARY} is not built; run "
                 "`python -m sandwich_norm_residual_amd.build` first")
+        # PyTorch first: it bundles its own HIP runtime under the same
+        # soname as the one libsnr.so links against, and a process keeps
+        # whichever copy it loads first. Loading ours ahead of torch's left
+        # later kernel launches failing with hipErrorNoDevice (100).
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIBRARY)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -148,6 +148,8 @@ def test_stream_probe_library_exports():
     """bench_stream.so (built by build()) loads without a GPU and exports its
     two entry points; the argument checks run before any HIP call."""
     import ctypes
+
+    import torch  # noqa: F401  (its HIP runtime before the library's)
     path = os.path.join(ROOT, "bench_stream.so")
     if not os.path.exists(path):
         pytest.skip("bench_stream.so not built")

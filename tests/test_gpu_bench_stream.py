@@ -1,0 +1,85 @@
+"""The benchmark's streaming kernels (bench_stream.hip): each variant touches
+exactly the bytes it is given, at every grid size bench.py uses, and the copy
+copies. Buffers carry guard bands on both sides that must stay untouched."""
+import ctypes
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PATH = os.path.join(ROOT, "bench_stream.so")
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096          # bytes on each side of the region
+READ, WRITE, WRITE_NT, COPY = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    # PyTorch's HIP runtime first: this library names the same runtime
+    # soname, and whichever copy a process loads first is the one it keeps.
+    import torch
+    torch.zeros(1, device="cuda:0")
+    if not os.path.exists(PATH):
+        pytest.fail(f"{PATH} is missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PATH)
+    L.stream_probe.restype = ctypes.c_int
+    L.stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_void_p]
+    return L
+
+
+def _buffers(torch, nbytes):
+    src = torch.randint(0, 256, (GUARD + nbytes + GUARD,), dtype=torch.uint8,
+                        device="cuda:0")
+    dst = torch.full((GUARD + nbytes + GUARD,), 0xA5, dtype=torch.uint8,
+                     device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    return src, dst, sink
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000003])
+@pytest.mark.parametrize("grid", [2048, 8192, 32768, 0, 1])
+def test_variants_touch_exactly_their_bytes(lib, nbytes, grid):
+    import torch
+    print(f"bench_stream nbytes={nbytes} grid={grid}", flush=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    for variant in (READ, WRITE, WRITE_NT, COPY):
+        src, dst, sink = _buffers(torch, nbytes)
+        before_src = src.clone()
+        rc = lib.stream_probe(variant, src.data_ptr() + GUARD,
+                              dst.data_ptr() + GUARD, sink.data_ptr(), nbytes,
+                              grid, stream)
+        assert rc == 0, (variant, rc)
+        torch.cuda.synchronize()
+        assert torch.equal(src, before_src), variant          # never written
+        assert (dst[:GUARD] == 0xA5).all() and (dst[-GUARD:] == 0xA5).all()
+        body = dst[GUARD:GUARD + nbytes]
+        if variant == READ:
+            assert (body == 0xA5).all()
+            assert int(sink[0]) in (0, 0x9E3779B9 - (1 << 32))
+        elif variant == COPY:
+            assert torch.equal(body, src[GUARD:GUARD + nbytes])
+        else:
+            # the fill (lane, 1, 2, 3) as f32: every 16-byte vector's last
+            # three words are 1.0, 2.0, 3.0
+            words = body.view(torch.float32).view(-1, 4).cpu()
+            assert (words[:, 1] == 1.0).all() and (words[:, 2] == 2.0).all()
+            assert (words[:, 3] == 3.0).all()
+            assert ((words[:, 0] >= 0) & (words[:, 0] < 256)).all()
+
+
+def test_invalid_arguments_enqueue_nothing(lib):
+    import torch
+    src, dst, sink = _buffers(torch, 64)
+    stream = torch.cuda.current_stream().cuda_stream
+    p = src.data_ptr() + GUARD
+    q = dst.data_ptr() + GUARD
+    assert lib.stream_probe(COPY, p, q, sink.data_ptr(), 24, 0, stream) == -1
+    assert lib.stream_probe(COPY, p + 4, q, sink.data_ptr(), 64, 0,
+                            stream) == -1
+    assert lib.stream_probe(7, p, q, sink.data_ptr(), 64, 0, stream) == -1
+    torch.cuda.synchronize()
+    assert (dst == 0xA5).all()
