@@ -87,7 +87,7 @@ def test_headline_scales_span_the_range():
     lr = np.log10(_row_rms(d["r"]))
     assert la.min() < -2.8 and la.max() > 1.8
     assert lr.min() < -0.9 and lr.max() > 0.9
-    # log-uniform: each decile of the range holds about a tenth of the rows
+    # log-uniform: each fifth of the range holds about a fifth of the rows
     counts, _ = np.histogram(la, bins=5, range=(-3, 2))
     assert counts.min() > 0.12 * len(la)
 
