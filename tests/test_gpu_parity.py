@@ -296,6 +296,48 @@ def test_bitwise_deterministic(name):
         assert np.array_equal(h1, h2) and np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("op,rows,n", [("plain", 1024, 65536),
+                                        ("tail", 512, 65536),
+                                        ("plain", 2000, 3 * 2048 * 4 + 5)])
+def test_split_repeated_runs_are_identical(oracle, op, rows, n):
+    """The split-row kernel is the one path whose workgroups wait on one
+    another. With more rows than can be co-resident (each workgroup walks
+    several rows), 40 back-to-back runs must give bit-identical outputs that
+    match the oracle, and no wait may have given up."""
+    say(f"split repeated op={op} rows={rows} n={n}")
+    if op == "plain":
+        inp = gen.random_plain(rows, n, 9300 + rows)
+        x, g = dev(inp["x"], "f32"), dev(inp["gamma"], "f32")
+        outs = [torch.full_like(x, float("nan"))]
+        call = lambda: snr.rmsnorm_fwd(x, g, inp["eps"], out=outs[0])  # noqa: E731
+    else:
+        inp = gen.random_tail(rows, n, 9400 + rows)
+        a, r = dev(inp["a"], "f32"), dev(inp["r"], "f32")
+        gp, gq = dev(inp["gamma_post"], "f32"), dev(inp["gamma_pre"], "f32")
+        outs = [torch.full_like(a, float("nan")), torch.full_like(a, float("nan"))]
+        call = lambda: snr.sandwich_tail(a, r, gp, inp["eps_post"], gq,  # noqa: E731
+                                         inp["eps_pre"], h_out=outs[0],
+                                         y_out=outs[1])
+    with snr.forced_shape("split", 0, 8):
+        call()
+        shape = snr.last_shape()
+        first = [o.clone() for o in outs]
+        for _ in range(39):
+            for o in outs:
+                o.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            for o, f in zip(outs, first):
+                assert torch.equal(o, f)
+    assert shape.startswith("split:256:8:4:"), shape
+    assert snr.split_timeouts() == 0
+    if op == "plain":
+        check_plain(oracle, inp, host_f64(first[0]), f"split-repeat-{n}")
+    else:
+        check_tail(oracle, inp, host_f64(first[0]), host_f64(first[1]),
+                   f"split-repeat-tail-{n}")
+
+
 def test_rows_zero_is_a_noop():
     say("rows=0")
     x = torch.empty(0, 64, device=DEV)
