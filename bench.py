@@ -74,7 +74,8 @@ PROBE_MIB = 256          # per stream and buffer set
 PROBE_GRIDS = (2048, 8192, 32768, 0)   # 0: one workgroup per trip's range
 
 
-def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
+def stream_ceiling(cfg, torch, stream, achieved_gbs: float, sets=None,
+                   shape: str = ""):
     """What plain streaming kernels (no arithmetic) sustain on this GPU, and
     the floor that sets for this workload's step.
 
@@ -99,6 +100,10 @@ def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
                                  ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_int64, ctypes.c_int,
                                  ctypes.c_void_p]
+    lib.stream_probe_rows.restype = ctypes.c_int
+    lib.stream_probe_rows.argtypes = [ctypes.c_void_p] * 4 + [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p]
     sink = torch.zeros(16, dtype=torch.int32, device="cuda:0")
     handle = stream.cuda_stream
 
@@ -141,6 +146,11 @@ def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
     copy_us = best_us(PROBE_COPY, buffers(w16), w16)
     floor_us = copy_us + (r_bytes - w_bytes) / rd * 1e-3
     floor_gbs = (r_bytes + w_bytes) / (floor_us * 1e-6) / 1e9
+    pattern = row_pattern(cfg, torch, stream, lib, sets, shape)
+    if pattern is not None:
+        pattern["achieved_frac_of_pattern"] = round(
+            achieved_gbs / ((r_bytes + w_bytes) / (pattern["us"] * 1e-6) /
+                            1e9), 4)
     return {"read_gbs": round(rd, 1), "write_gbs": round(wr, 1),
             "copy_gbs": round(2 * w16 / copy_us * 1e-3, 1),
             "copy_us": round(copy_us, 3),
@@ -149,11 +159,57 @@ def stream_ceiling(cfg, torch, stream, achieved_gbs: float):
             "floor_frac_of_peak": round(floor_gbs / PEAK_HBM_GBS, 4),
             "achieved_frac_of_floor": round(achieved_gbs / floor_gbs, 4),
             "model": "copy of W bytes in one launch + (R - W) / read_gbs",
+            "row_pattern": pattern,
             "probe": (f"plain read / write / copy kernels "
                       f"(bench_stream.hip); copy of the step's written "
                       f"bytes over rotating sets of >= 1 GiB; read and "
                       f"write over {PROBE_MIB} MiB buffers; best of grids "
                       f"{list(PROBE_GRIDS)} (0 = one trip)")}
+
+
+ROW_PATTERN_SHAPES = {(1024, 1), (1024, 2), (512, 2), (512, 4), (256, 4),
+                      (256, 8)}
+
+
+def row_pattern(cfg, torch, stream, lib, sets, shape: str):
+    """The step's own access pattern with no arithmetic, on the step's own
+    buffers: for the two-read, two-write operations (the tail and
+    add_then_norm) run by a one-row-per-workgroup tile, a kernel that loads
+    both input rows and stores both outputs, one row per workgroup of the
+    same lanes and vectors per lane. None for other workloads."""
+    parts = shape.split(":")
+    if (cfg.kind not in ("tail", "add_norm") or not sets or len(parts) != 4
+            or parts[0] not in ("rowtile", "persist")):
+        return None
+    lanes, vpt, width = int(parts[1]), int(parts[2]), int(parts[3])
+    if (lanes, vpt) not in ROW_PATTERN_SHAPES or cfg.n % width:
+        return None
+    keys = ("a", "r") if cfg.kind == "tail" else ("a", "b")
+    handle = stream.cuda_stream
+
+    def launch(i):
+        st = sets[i % len(sets)]
+        rc = lib.stream_probe_rows(st[keys[0]].data_ptr(),
+                                   st[keys[1]].data_ptr(),
+                                   st["out"][0].data_ptr(),
+                                   st["out"][1].data_ptr(), cfg.rows,
+                                   cfg.n // width, lanes, vpt, handle)
+        if rc != 0:
+            raise RuntimeError(f"stream_probe_rows -> {rc}")
+    with torch.cuda.stream(stream):
+        for i in range(5):
+            launch(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(200):
+            launch(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return {"us": round(e0.elapsed_time(e1) * 1e3 / 200, 3),
+            "lanes": lanes, "vectors_per_lane": vpt,
+            "what": "both input rows loaded, both outputs stored, one row "
+                    "per workgroup, no arithmetic (bench_stream.hip)"}
 
 
 def kernel_sources(cfg) -> list:
@@ -507,13 +563,18 @@ def main() -> int:
     # the floor needs an HBM-bound step: at least 64 MiB of traffic
     ceiling = None
     if not args.no_ceiling and nbytes >= (64 << 20):
-        ceiling = stream_ceiling(cfg, torch, stream, achieved)
+        ceiling = stream_ceiling(cfg, torch, stream, achieved, sets, shape)
         log(f"attainable: read {ceiling['read_gbs']} GB/s, write "
             f"{ceiling['write_gbs']} GB/s, copy of the step's written bytes "
             f"{ceiling['copy_us']} us = {ceiling['copy_gbs']} GB/s; "
             f"floor {ceiling['floor_us']} us/step = "
             f"{100 * ceiling['floor_frac_of_peak']:.1f}% of peak; this step "
             f"reaches {100 * ceiling['achieved_frac_of_floor']:.1f}% of it")
+        if ceiling["row_pattern"]:
+            pat = ceiling["row_pattern"]
+            log(f"row pattern without arithmetic ({pat['lanes']} x "
+                f"{pat['vectors_per_lane']}): {pat['us']} us; this step "
+                f"reaches {100 * pat['achieved_frac_of_pattern']:.1f}% of it")
 
     cpu = None
     if not args.no_cpu:

@@ -1,19 +1,27 @@
-// Streaming kernels that measure what this GPU's HBM sustains for plain reads,
-// plain writes and plain copies, with no arithmetic and no reduction. The
-// benchmark times them beside the hot path to state the attainable floor for
-// a workload's own mix of reads and writes: an HBM channel carries reads or
-// writes at any one moment, never both, so moving R bytes in and W bytes out
-// takes at least R / (best read rate) + W / (best write rate).
+// Streaming kernels that the benchmark times beside the hot path, to state
+// what this GPU's HBM sustains for the same bytes with no arithmetic and no
+// reduction:
+// * plain reads, plain writes and plain copies (stream_probe). Reads alone
+//   and writes alone each stream faster than any mix of the two (an HBM
+//   channel turns its bus around between them), so a step's floor is a
+//   plain copy of its written bytes plus its remaining reads at the
+//   read-only rate;
+// * the access pattern of a two-read, two-write row operation
+//   (stream_probe_rows): one row per workgroup, as the row-tile kernels lay
+//   it out, loads then stores, nothing computed.
 //
 // Not part of the library: built into bench_stream.so, loaded by bench.py
 // only.
 //
-// Access pattern: a flat grid-stride loop over 16-byte vectors, 256 lanes per
-// workgroup, U vectors per lane per trip spaced 256 vectors apart, so that a
-// workgroup touches 256*U consecutive vectors per trip and consecutive
-// workgroups touch consecutive ranges. Every access is guarded by i < total.
+// stream_probe's access pattern: a flat grid-stride loop over 16-byte
+// vectors, 256 lanes per workgroup, U vectors per lane per trip spaced 256
+// vectors apart, so that a workgroup touches 256*U consecutive vectors per
+// trip and consecutive workgroups touch consecutive ranges. Every access is
+// guarded by i < total.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <initializer_list>
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
@@ -85,6 +93,34 @@ __global__ void __launch_bounds__(kLanes) copy_kernel(const f4 *src, f4 *dst, in
     }
 }
 
+// The access pattern of a two-read, two-write row operation (the fused tail,
+// add_then_norm) with no arithmetic: one row per workgroup of LANES lanes,
+// VPT vectors per lane of each stream, consecutive lanes on consecutive
+// vectors; both rows are loaded, then the two outputs are stored.
+template <int LANES, int VPT>
+__global__ void __launch_bounds__(LANES) rows_kernel(const f4 *a, const f4 *r, f4 *h, f4 *y, int nvec) {
+    const int64_t o = (int64_t)blockIdx.x * nvec;
+    f4 va[VPT], vr[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int i = k * LANES + (int)threadIdx.x;
+        if (i < nvec) {
+            va[k] = load<true>(a + o + i);
+            vr[k] = load<true>(r + o + i);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int i = k * LANES + (int)threadIdx.x;
+        if (i < nvec) store<true>(va[k] + vr[k], h + o + i);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int i = k * LANES + (int)threadIdx.x;
+        if (i < nvec) store<true>(va[k] - vr[k], y + o + i);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +157,32 @@ int stream_probe(int variant, const void *src, void *dst, unsigned *sink, int64_
     case 2: write_kernel<true, 1><<<(unsigned)g, kLanes, 0, stream>>>(d, total); break;
     default: copy_kernel<true, 4><<<(unsigned)g, kLanes, 0, stream>>>(s, d, total); break;
     }
+    return (int)hipGetLastError();
+}
+
+// Enqueues the two-read, two-write row pattern on `stream`: rows of `nvec`
+// 16-byte vectors in a, r (read) and h, y (written), one workgroup of `lanes`
+// lanes per row with `vpt` vectors per lane of each stream. (lanes, vpt) is
+// one of (1024, 1), (1024, 2), (512, 2), (512, 4), (256, 4), (256, 8), and
+// lanes * vpt must cover nvec. Pointers are device pointers aligned to 16
+// bytes. Returns 0, -1 for an invalid argument (nothing enqueued) or the HIP
+// error of the launch.
+int stream_probe_rows(const void *a, const void *r, void *h, void *y, int64_t rows, int64_t nvec, int lanes,
+                      int vpt, hipStream_t stream) {
+    if (rows <= 0 || rows > 0x7fffffff || nvec <= 0 || nvec > (int64_t)lanes * vpt) return -1;
+    for (const void *p : {a, (const void *)r, (const void *)h, (const void *)y})
+        if (!p || (uintptr_t)p % 16) return -1;
+    const f4 *fa = static_cast<const f4 *>(a), *fr = static_cast<const f4 *>(r);
+    f4 *fh = static_cast<f4 *>(h), *fy = static_cast<f4 *>(y);
+    const int nv = (int)nvec;
+    const unsigned g = (unsigned)rows;
+    if (lanes == 1024 && vpt == 1) rows_kernel<1024, 1><<<g, 1024, 0, stream>>>(fa, fr, fh, fy, nv);
+    else if (lanes == 1024 && vpt == 2) rows_kernel<1024, 2><<<g, 1024, 0, stream>>>(fa, fr, fh, fy, nv);
+    else if (lanes == 512 && vpt == 2) rows_kernel<512, 2><<<g, 512, 0, stream>>>(fa, fr, fh, fy, nv);
+    else if (lanes == 512 && vpt == 4) rows_kernel<512, 4><<<g, 512, 0, stream>>>(fa, fr, fh, fy, nv);
+    else if (lanes == 256 && vpt == 4) rows_kernel<256, 4><<<g, 256, 0, stream>>>(fa, fr, fh, fy, nv);
+    else if (lanes == 256 && vpt == 8) rows_kernel<256, 8><<<g, 256, 0, stream>>>(fa, fr, fh, fy, nv);
+    else return -1;
     return (int)hipGetLastError();
 }
 

@@ -83,3 +83,54 @@ def test_invalid_arguments_enqueue_nothing(lib):
     assert lib.stream_probe(7, p, q, sink.data_ptr(), 64, 0, stream) == -1
     torch.cuda.synchronize()
     assert (dst == 0xA5).all()
+
+
+@pytest.mark.parametrize("lanes,vpt,nvec", [(1024, 2, 1664), (1024, 1, 1000),
+                                            (512, 2, 832), (512, 4, 2048),
+                                            (256, 4, 7), (256, 8, 2048)])
+def test_row_pattern_touches_exactly_its_rows(lib, lanes, vpt, nvec):
+    """stream_probe_rows: h = a + r and y = a - r on every vector of every
+    row, nothing outside the four [rows, nvec] regions."""
+    import torch
+    lib.stream_probe_rows.restype = ctypes.c_int
+    lib.stream_probe_rows.argtypes = [ctypes.c_void_p] * 4 + [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p]
+    rows = 37
+    print(f"bench_stream rows={rows} nvec={nvec} lanes={lanes} vpt={vpt}",
+          flush=True)
+    g = GUARD // 4
+    m = rows * nvec * 4
+    a = torch.randn(g + m + g, device="cuda:0")
+    r = torch.randn(g + m + g, device="cuda:0")
+    h = torch.full((g + m + g,), 7.0, device="cuda:0")
+    y = torch.full((g + m + g,), 7.0, device="cuda:0")
+    a0, r0 = a.clone(), r.clone()
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = lib.stream_probe_rows(a.data_ptr() + GUARD, r.data_ptr() + GUARD,
+                               h.data_ptr() + GUARD, y.data_ptr() + GUARD,
+                               rows, nvec, lanes, vpt, stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(a, a0) and torch.equal(r, r0)
+    for t in (h, y):
+        assert (t[:g] == 7.0).all() and (t[g + m:] == 7.0).all()
+    assert torch.equal(h[g:g + m], a[g:g + m] + r[g:g + m])
+    assert torch.equal(y[g:g + m], a[g:g + m] - r[g:g + m])
+
+
+def test_row_pattern_rejects_what_it_cannot_cover(lib):
+    import torch
+    lib.stream_probe_rows.restype = ctypes.c_int
+    lib.stream_probe_rows.argtypes = [ctypes.c_void_p] * 4 + [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p]
+    t = torch.zeros(4096, device="cuda:0")
+    p = t.data_ptr()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.stream_probe_rows(p, p, p, p, 1, 2049, 1024, 2, stream) == -1
+    assert lib.stream_probe_rows(p, p, p, p, 1, 64, 128, 2, stream) == -1
+    assert lib.stream_probe_rows(p + 4, p, p, p, 1, 64, 256, 4, stream) == -1
+    assert lib.stream_probe_rows(p, p, p, p, 0, 64, 256, 4, stream) == -1
+    torch.cuda.synchronize()
+    assert (t == 0).all()
