@@ -168,9 +168,16 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     // Only the f16 header uses 1/rms, so the hardware reciprocal square root
     // (about one f32 unit) replaces IEEE square root and division: a shorter
     // chain between a row's reduction and its stores.
+    // v_rsq_f32 takes a subnormal input as zero. The input is below the
+    // smallest normal only when epsilon is subnormal; it is then scaled by
+    // 2^24 and the result by 2^12, both exact, so a zero row still gets a
+    // finite 1/rms (and d = 0).
     const float inv_n = 1.0f / (float)p.n;
     auto inverse_rms = [&](float s, float *slot) {
-        return __builtin_amdgcn_rsqf(fmaf(row_total<G>(s, slot), inv_n, p.eps0));
+        const float v = fmaf(row_total<G>(s, slot), inv_n, p.eps0);
+        const bool tiny = v < 0x1p-126f;
+        const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p24f : v);
+        return tiny ? r * 0x1p12f : r;
     };
 
     const int lrow = threadIdx.x / G;

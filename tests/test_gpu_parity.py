@@ -338,6 +338,36 @@ def test_split_repeated_runs_are_identical(oracle, op, rows, n):
                    f"split-repeat-tail-{n}")
 
 
+@pytest.mark.parametrize("n", [6656, 6657, 3])
+def test_subnormal_epsilon(oracle, n):
+    """epsilon = the smallest f32 subnormal (2^-149) on both norms: zero rows
+    give exactly 0 and h = r, and rows whose mean square plus epsilon is
+    below the smallest normal match the oracle."""
+    say(f"subnormal epsilon n={n}")
+    eps = float(np.float32(2.0 ** -149))
+    inp = gen.random_plain(6, n, 9500 + n)
+    inp["eps"] = eps
+    x = inp["x"]
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, n // 2] = np.float32(1e-18)      # mean square below 2^-126
+    got, _ = run_plain(inp)
+    check_plain(oracle, inp, got, f"subnormal-eps-plain-{n}")
+    assert not got[0].any()
+    tin = gen.random_tail(4, n, 9600 + n)
+    tin["eps_post"] = tin["eps_pre"] = eps
+    tin["a"][0] = 0.0                     # h = r, y = rmsnorm(r)
+    tin["a"][1] = 0.0
+    tin["r"][1] = 0.0                     # h = 0, y = 0
+    tin["a"][2] = 0.0
+    tin["a"][2, 0] = np.float32(1e-18)
+    tin["r"][2] = 0.0                     # h and y from a tiny post-norm
+    h, y = run_tail(tin)
+    check_tail(oracle, tin, h, y, f"subnormal-eps-tail-{n}")
+    assert np.array_equal(h[0], tin["r"][0].astype(np.float64))
+    assert not h[1].any() and not y[1].any()
+
+
 def test_rows_zero_is_a_noop():
     say("rows=0")
     x = torch.empty(0, 64, device=DEV)

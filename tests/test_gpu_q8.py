@@ -135,6 +135,31 @@ def test_tiny_blocks_and_subnormal_inputs(oracle):
     assert int(q[0, 0].abs().max()) == 127      # the block's own scale
 
 
+@pytest.mark.parametrize("st", ["f32", "bf16"])
+def test_subnormal_epsilon(oracle, st):
+    """epsilon = the smallest f32 subnormal (2^-149): a zero row still
+    encodes d = 0 and q = 0 (1/rms stays finite), and rows whose mean square
+    plus epsilon falls below the smallest normal match the oracle."""
+    say(f"q8 subnormal epsilon {st}")
+    rng = gen.rng_for(28200)
+    rows, n = 5, 256
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 37] = np.float32(1e-18)          # mean square 1e-36 / 256 < 2^-126
+    x[2] *= np.float32(1e-20)             # squares near 1e-40 ... 1e-39
+    x[2] = np.where(np.abs(x[2]) < 1e-20, np.float32(1e-20), x[2])
+    x[3, 64:] = 0.0                       # zero blocks after normal ones
+    g = (1.0 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    eps = float(np.float32(2.0 ** -149))
+    inp = {"x": gen.to_storage(x, st), "gamma": gen.to_storage(g, st),
+           "eps": eps, "dtype": st}
+    blocks = run_q8(inp)
+    check_q8(oracle, inp, blocks, f"q8-subnormal-eps-{st}")
+    assert not blocks[0].any()
+    assert not blocks[3, 2:].any()
+
+
 def test_exact_ties_round_to_even(oracle):
     """A block whose quotients x / d are exact ties (rms = 64 and d = 1/32
     exactly, t = x / 2): the codes are round-half-even of the exact
