@@ -84,7 +84,9 @@ enum {
  *
  *   x      [rows, n] input, dtype `dtype`, device memory
  *   gamma  [n] per-channel gain, same dtype as x
- *   eps    epsilon added to the mean of squares; finite and > 0
+ *   eps    epsilon added to the mean of squares; finite and > 0 (a
+ *          subnormal epsilon is computed; one so large that the mean of
+ *          squares plus epsilon overflows f32 gives 1/rms = 0)
  *   rows   number of rows (>= 0)
  *   n      row width (>= 1)
  *   dtype  SNR_F32, SNR_BF16 or SNR_F16 (storage of x, gamma and y)
