@@ -167,33 +167,36 @@ def stream_ceiling(cfg, torch, stream, achieved_gbs: float, sets=None,
                       f"{list(PROBE_GRIDS)} (0 = one trip)")}
 
 
-ROW_PATTERN_SHAPES = {(1024, 1), (1024, 2), (512, 2), (512, 4), (256, 4),
-                      (256, 8)}
+ROW_PATTERN_SHAPES = {(1024, 1), (1024, 2), (512, 2), (512, 4), (256, 2),
+                      (256, 4), (256, 8)}
+# input row streams of each operation with a row pattern (outputs: out[...])
+ROW_PATTERN_INPUTS = {"plain": ("x",), "norm_add": ("a", "b"),
+                      "tail": ("a", "r"), "add_norm": ("a", "b")}
 
 
 def row_pattern(cfg, torch, stream, lib, sets, shape: str):
     """The step's own access pattern with no arithmetic, on the step's own
-    buffers: for the two-read, two-write operations (the tail and
-    add_then_norm) run by a one-row-per-workgroup tile, a kernel that loads
-    both input rows and stores both outputs, one row per workgroup of the
-    same lanes and vectors per lane. None for other workloads."""
+    buffers: for an operation run by a one-row-per-workgroup tile, a kernel
+    that loads its input rows and stores its output rows, one row per
+    workgroup of the same lanes and vectors per lane. None for other
+    workloads and shapes."""
     parts = shape.split(":")
-    if (cfg.kind not in ("tail", "add_norm") or not sets or len(parts) != 4
+    if (cfg.kind not in ROW_PATTERN_INPUTS or not sets or len(parts) != 4
             or parts[0] not in ("rowtile", "persist")):
         return None
     lanes, vpt, width = int(parts[1]), int(parts[2]), int(parts[3])
     if (lanes, vpt) not in ROW_PATTERN_SHAPES or cfg.n % width:
         return None
-    keys = ("a", "r") if cfg.kind == "tail" else ("a", "b")
+    keys = ROW_PATTERN_INPUTS[cfg.kind]
     handle = stream.cuda_stream
 
     def launch(i):
         st = sets[i % len(sets)]
-        rc = lib.stream_probe_rows(st[keys[0]].data_ptr(),
-                                   st[keys[1]].data_ptr(),
-                                   st["out"][0].data_ptr(),
-                                   st["out"][1].data_ptr(), cfg.rows,
-                                   cfg.n // width, lanes, vpt, handle)
+        ins = [st[k].data_ptr() for k in keys] + [None]
+        outs = [o.data_ptr() for o in st["out"]] + [None]
+        rc = lib.stream_probe_rows(ins[0], ins[1], outs[0], outs[1],
+                                   cfg.rows, cfg.n // width, lanes, vpt,
+                                   handle)
         if rc != 0:
             raise RuntimeError(f"stream_probe_rows -> {rc}")
     with torch.cuda.stream(stream):
@@ -208,8 +211,9 @@ def row_pattern(cfg, torch, stream, lib, sets, shape: str):
     torch.cuda.synchronize()
     return {"us": round(e0.elapsed_time(e1) * 1e3 / 200, 3),
             "lanes": lanes, "vectors_per_lane": vpt,
-            "what": "both input rows loaded, both outputs stored, one row "
-                    "per workgroup, no arithmetic (bench_stream.hip)"}
+            "what": f"{len(keys)} input row(s) loaded, {len(sets[0]['out'])} "
+                    "output row(s) stored, one row per workgroup, no "
+                    "arithmetic (bench_stream.hip)"}
 
 
 def kernel_sources(cfg) -> list:

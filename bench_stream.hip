@@ -6,9 +6,9 @@
 //   channel turns its bus around between them), so a step's floor is a
 //   plain copy of its written bytes plus its remaining reads at the
 //   read-only rate;
-// * the access pattern of a two-read, two-write row operation
-//   (stream_probe_rows): one row per workgroup, as the row-tile kernels lay
-//   it out, loads then stores, nothing computed.
+// * the access pattern of a row operation (stream_probe_rows): one or two
+//   input rows and one or two output rows per workgroup, as the row-tile
+//   kernels lay them out, loads then stores, nothing computed.
 //
 // Not part of the library: built into bench_stream.so, loaded by bench.py
 // only.
@@ -93,11 +93,11 @@ __global__ void __launch_bounds__(kLanes) copy_kernel(const f4 *src, f4 *dst, in
     }
 }
 
-// The access pattern of a two-read, two-write row operation (the fused tail,
-// add_then_norm) with no arithmetic: one row per workgroup of LANES lanes,
-// VPT vectors per lane of each stream, consecutive lanes on consecutive
-// vectors; both rows are loaded, then the two outputs are stored.
-template <int LANES, int VPT>
+// The access pattern of a row operation with no arithmetic: one row per
+// workgroup of LANES lanes, VPT vectors per lane of each stream, consecutive
+// lanes on consecutive vectors; the input rows (a, and r when TWO_IN) are
+// loaded, then the outputs (h, and y when TWO_OUT) are stored.
+template <int LANES, int VPT, bool TWO_IN, bool TWO_OUT>
 __global__ void __launch_bounds__(LANES) rows_kernel(const f4 *a, const f4 *r, f4 *h, f4 *y, int nvec) {
     const int64_t o = (int64_t)blockIdx.x * nvec;
     f4 va[VPT], vr[VPT];
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(LANES) rows_kernel(const f4 *a, const f4 *r, f
         const int i = k * LANES + (int)threadIdx.x;
         if (i < nvec) {
             va[k] = load<true>(a + o + i);
-            vr[k] = load<true>(r + o + i);
+            vr[k] = TWO_IN ? load<true>(r + o + i) : va[k];
         }
     }
 #pragma unroll
@@ -114,11 +114,27 @@ __global__ void __launch_bounds__(LANES) rows_kernel(const f4 *a, const f4 *r, f
         const int i = k * LANES + (int)threadIdx.x;
         if (i < nvec) store<true>(va[k] + vr[k], h + o + i);
     }
+    if constexpr (TWO_OUT) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int i = k * LANES + (int)threadIdx.x;
-        if (i < nvec) store<true>(va[k] - vr[k], y + o + i);
+        for (int k = 0; k < VPT; ++k) {
+            const int i = k * LANES + (int)threadIdx.x;
+            if (i < nvec) store<true>(va[k] - vr[k], y + o + i);
+        }
     }
+}
+
+template <bool TWO_IN, bool TWO_OUT>
+int launch_rows(const f4 *a, const f4 *r, f4 *h, f4 *y, unsigned rows, int nvec, int lanes, int vpt,
+                hipStream_t stream) {
+    if (lanes == 1024 && vpt == 1) rows_kernel<1024, 1, TWO_IN, TWO_OUT><<<rows, 1024, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 1024 && vpt == 2) rows_kernel<1024, 2, TWO_IN, TWO_OUT><<<rows, 1024, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 512 && vpt == 2) rows_kernel<512, 2, TWO_IN, TWO_OUT><<<rows, 512, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 512 && vpt == 4) rows_kernel<512, 4, TWO_IN, TWO_OUT><<<rows, 512, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 256 && vpt == 2) rows_kernel<256, 2, TWO_IN, TWO_OUT><<<rows, 256, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 256 && vpt == 4) rows_kernel<256, 4, TWO_IN, TWO_OUT><<<rows, 256, 0, stream>>>(a, r, h, y, nvec);
+    else if (lanes == 256 && vpt == 8) rows_kernel<256, 8, TWO_IN, TWO_OUT><<<rows, 256, 0, stream>>>(a, r, h, y, nvec);
+    else return -1;
+    return (int)hipGetLastError();
 }
 
 }  // namespace
@@ -160,30 +176,28 @@ int stream_probe(int variant, const void *src, void *dst, unsigned *sink, int64_
     return (int)hipGetLastError();
 }
 
-// Enqueues the two-read, two-write row pattern on `stream`: rows of `nvec`
-// 16-byte vectors in a, r (read) and h, y (written), one workgroup of `lanes`
-// lanes per row with `vpt` vectors per lane of each stream. (lanes, vpt) is
-// one of (1024, 1), (1024, 2), (512, 2), (512, 4), (256, 4), (256, 8), and
+// Enqueues a row operation's access pattern with no arithmetic on `stream`:
+// rows of `nvec` 16-byte vectors, read from a (and r, if not NULL) and
+// written to h (and y, if not NULL), one workgroup of `lanes` lanes per row
+// with `vpt` vectors per lane of each stream. (lanes, vpt) is one of
+// (1024, 1), (1024, 2), (512, 2), (512, 4), (256, 2), (256, 4), (256, 8), and
 // lanes * vpt must cover nvec. Pointers are device pointers aligned to 16
 // bytes. Returns 0, -1 for an invalid argument (nothing enqueued) or the HIP
 // error of the launch.
 int stream_probe_rows(const void *a, const void *r, void *h, void *y, int64_t rows, int64_t nvec, int lanes,
                       int vpt, hipStream_t stream) {
     if (rows <= 0 || rows > 0x7fffffff || nvec <= 0 || nvec > (int64_t)lanes * vpt) return -1;
+    if (!a || !h) return -1;
     for (const void *p : {a, (const void *)r, (const void *)h, (const void *)y})
-        if (!p || (uintptr_t)p % 16) return -1;
+        if ((uintptr_t)p % 16) return -1;
     const f4 *fa = static_cast<const f4 *>(a), *fr = static_cast<const f4 *>(r);
     f4 *fh = static_cast<f4 *>(h), *fy = static_cast<f4 *>(y);
     const int nv = (int)nvec;
     const unsigned g = (unsigned)rows;
-    if (lanes == 1024 && vpt == 1) rows_kernel<1024, 1><<<g, 1024, 0, stream>>>(fa, fr, fh, fy, nv);
-    else if (lanes == 1024 && vpt == 2) rows_kernel<1024, 2><<<g, 1024, 0, stream>>>(fa, fr, fh, fy, nv);
-    else if (lanes == 512 && vpt == 2) rows_kernel<512, 2><<<g, 512, 0, stream>>>(fa, fr, fh, fy, nv);
-    else if (lanes == 512 && vpt == 4) rows_kernel<512, 4><<<g, 512, 0, stream>>>(fa, fr, fh, fy, nv);
-    else if (lanes == 256 && vpt == 4) rows_kernel<256, 4><<<g, 256, 0, stream>>>(fa, fr, fh, fy, nv);
-    else if (lanes == 256 && vpt == 8) rows_kernel<256, 8><<<g, 256, 0, stream>>>(fa, fr, fh, fy, nv);
-    else return -1;
-    return (int)hipGetLastError();
+    if (r && y) return launch_rows<true, true>(fa, fr, fh, fy, g, nv, lanes, vpt, stream);
+    if (r) return launch_rows<true, false>(fa, fr, fh, fy, g, nv, lanes, vpt, stream);
+    if (y) return launch_rows<false, true>(fa, fr, fh, fy, g, nv, lanes, vpt, stream);
+    return launch_rows<false, false>(fa, fr, fh, fy, g, nv, lanes, vpt, stream);
 }
 
 }  // extern "C"

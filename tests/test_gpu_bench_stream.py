@@ -85,20 +85,25 @@ def test_invalid_arguments_enqueue_nothing(lib):
     assert (dst == 0xA5).all()
 
 
+@pytest.mark.parametrize("two_in,two_out", [(True, True), (True, False),
+                                            (False, False), (False, True)])
 @pytest.mark.parametrize("lanes,vpt,nvec", [(1024, 2, 1664), (1024, 1, 1000),
                                             (512, 2, 832), (512, 4, 2048),
-                                            (256, 4, 7), (256, 8, 2048)])
-def test_row_pattern_touches_exactly_its_rows(lib, lanes, vpt, nvec):
-    """stream_probe_rows: h = a + r and y = a - r on every vector of every
-    row, nothing outside the four [rows, nvec] regions."""
+                                            (256, 2, 512), (256, 4, 7),
+                                            (256, 8, 2048)])
+def test_row_pattern_touches_exactly_its_rows(lib, lanes, vpt, nvec, two_in,
+                                              two_out):
+    """stream_probe_rows: h = a + r and y = a - r (r = a without a second
+    input) on every vector of every row, nothing outside the [rows, nvec]
+    regions, and no stream that was not passed is touched."""
     import torch
     lib.stream_probe_rows.restype = ctypes.c_int
     lib.stream_probe_rows.argtypes = [ctypes.c_void_p] * 4 + [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p]
     rows = 37
-    print(f"bench_stream rows={rows} nvec={nvec} lanes={lanes} vpt={vpt}",
-          flush=True)
+    print(f"bench_stream rows={rows} nvec={nvec} lanes={lanes} vpt={vpt} "
+          f"two_in={two_in} two_out={two_out}", flush=True)
     g = GUARD // 4
     m = rows * nvec * 4
     a = torch.randn(g + m + g, device="cuda:0")
@@ -107,16 +112,23 @@ def test_row_pattern_touches_exactly_its_rows(lib, lanes, vpt, nvec):
     y = torch.full((g + m + g,), 7.0, device="cuda:0")
     a0, r0 = a.clone(), r.clone()
     stream = torch.cuda.current_stream().cuda_stream
-    rc = lib.stream_probe_rows(a.data_ptr() + GUARD, r.data_ptr() + GUARD,
-                               h.data_ptr() + GUARD, y.data_ptr() + GUARD,
+    rc = lib.stream_probe_rows(a.data_ptr() + GUARD,
+                               r.data_ptr() + GUARD if two_in else None,
+                               h.data_ptr() + GUARD,
+                               y.data_ptr() + GUARD if two_out else None,
                                rows, nvec, lanes, vpt, stream)
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(a, a0) and torch.equal(r, r0)
     for t in (h, y):
         assert (t[:g] == 7.0).all() and (t[g + m:] == 7.0).all()
-    assert torch.equal(h[g:g + m], a[g:g + m] + r[g:g + m])
-    assert torch.equal(y[g:g + m], a[g:g + m] - r[g:g + m])
+    body = slice(g, g + m)
+    second = r[body] if two_in else a[body]
+    assert torch.equal(h[body], a[body] + second)
+    if two_out:
+        assert torch.equal(y[body], a[body] - second)
+    else:
+        assert (y == 7.0).all()
 
 
 def test_row_pattern_rejects_what_it_cannot_cover(lib):
@@ -132,5 +144,7 @@ def test_row_pattern_rejects_what_it_cannot_cover(lib):
     assert lib.stream_probe_rows(p, p, p, p, 1, 64, 128, 2, stream) == -1
     assert lib.stream_probe_rows(p + 4, p, p, p, 1, 64, 256, 4, stream) == -1
     assert lib.stream_probe_rows(p, p, p, p, 0, 64, 256, 4, stream) == -1
+    assert lib.stream_probe_rows(None, p, p, p, 1, 64, 256, 4, stream) == -1
+    assert lib.stream_probe_rows(p, p, None, p, 1, 64, 256, 4, stream) == -1
     torch.cuda.synchronize()
     assert (t == 0).all()
