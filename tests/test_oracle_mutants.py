@@ -5,7 +5,8 @@ temporary library; the pins of ``oracle_pins.py`` are run against it and at
 least one of them must fail. This shows the pins can go red for each class of
 error (epsilon placement, divisor, dropped tail elements, dropped gain, sign
 of the residual add, which epsilon and which gain each norm of the tail uses,
-the row stride, the bf16 decode). CPU only: the mistakes are planted in the
+the row stride, the bf16 decode, f32 accumulation, a skipped element, a
+missing root, and the Q8_1 block rules). CPU only: the mistakes are planted in the
 oracle, never in GPU code.
 """
 import os
@@ -25,6 +26,11 @@ MUTANTS = {
     "drop_ragged_tail": ("    for (int64_t j = 0; j < n; ++j)\n        sum_sq += x[j] * x[j];",
                          "    for (int64_t j = 0; j < (n & ~(int64_t)3); ++j)\n        sum_sq += x[j] * x[j];"),
     "sum_abs_not_squares": ("sum_sq += x[j] * x[j];", "sum_sq += fabs(x[j]);"),
+    "sum_in_float": ("double sum_sq = 0.0;", "float sum_sq = 0.0f;"),
+    "sum_skips_first": ("    for (int64_t j = 0; j < n; ++j)\n        sum_sq += x[j] * x[j];",
+                        "    for (int64_t j = 1; j < n; ++j)\n        sum_sq += x[j] * x[j];"),
+    "rms_without_root": ("const double rms = sqrt(mean_sq + eps);",
+                         "const double rms = mean_sq + eps;"),
     "drop_gain": ("y[j] = x[j] / rms * gamma[j];", "y[j] = x[j] / rms;"),
     "multiply_by_rms": ("y[j] = x[j] / rms * gamma[j];", "y[j] = x[j] * rms * gamma[j];"),
     "residual_sign": ("hi[j] = (double)r[i * n + j] + p[j];",
