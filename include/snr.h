@@ -53,7 +53,8 @@ typedef enum {
 /* Every operation reads its storage type exactly into f32, accumulates and
  * computes in f32, and rounds its outputs to the storage type to nearest
  * even. An intermediate that a later norm of the same call reads (the
- * tail's h, add_then_norm's sum) is normalised as it is stored. */
+ * tail's h, add_then_norm's sum) is stored rounded to the storage type,
+ * and the later norm works from its f32 value, so y carries one rounding. */
 
 enum {
     SNR_OK = 0,
@@ -140,7 +141,11 @@ SNR_API int sandwich_tail(const float *a, const float *r, const float *gamma_pos
 /*
  * sandwich_tail_typed - the same tail for any snr_dtype storage: a, r, both
  * gains, h_out and y_out all of type `dtype`. With bf16 or f16 storage, h is
- * rounded to the storage type before its norm (y = norm of h as stored).
+ * stored rounded to the storage type, and y is the norm of its f32 value
+ * (one rounding in y; normalising the rounded copy would add the rounding
+ * of the row's largest element to every output). Rows too wide for the
+ * split-row kernel (beyond about 6 million elements) go through multi-pass
+ * kernels whose last pass re-reads the stored h: there y carries two.
  * Same aliasing rules as sandwich_tail.
  *
  * sandwich_tail_inplace - the tail with the residual stream updated in place
@@ -186,7 +191,8 @@ SNR_API int norm_then_add(const void *a, const void *r, const void *gamma,
  *   a, b      [rows, n] of `dtype`;  gamma [n] of `dtype`
  *   sum_out   [rows, n]; may coincide exactly with a or with b
  *   y_out     [rows, n]; may overlap no other buffer
- * With bf16 or f16 storage, y is the norm of the sum as stored.
+ * With bf16 or f16 storage, the sum is stored rounded and y is the norm
+ * of its f32 value.
  */
 SNR_API int add_then_norm(const void *a, const void *b, const void *gamma,
                           float eps, void *sum_out, void *y_out, int64_t rows,

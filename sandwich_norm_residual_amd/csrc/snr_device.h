@@ -22,7 +22,6 @@ namespace {
 // (16-bit types) boundary, so rows whose start is not 16-byte aligned (odd
 // n, offset views) still use 128-bit accesses. The n % W elements after a
 // row's last whole vector are moved one at a time.
-// `round` rounds an f32 value to the storage type and back (exact decode).
 // ---------------------------------------------------------------------------
 template <int ST>
 struct Codec;
@@ -65,7 +64,6 @@ struct Codec<ST_F32> {
     __device__ static void store1_nt(T *row, int j, float v) {
         __builtin_nontemporal_store(v, row + j);
     }
-    __device__ static float round(float v) { return v; }
 };
 
 // Two 16-bit values per 32-bit word, element 2k in the low half.
@@ -169,7 +167,6 @@ struct Codec16 {
     __device__ static void store1_nt(T *row, int j, float v) {
         __builtin_nontemporal_store(B::enc(v), row + j);
     }
-    __device__ static float round(float v) { return B::one(B::enc(v)); }
 };
 
 template <>

@@ -12,8 +12,10 @@
 //   add_then_norm (Hesper residualAddRmsNormKernel):
 //       s = a + b;  y = s / sqrt(mean(s^2) + eps) * gamma   (writes s and y)
 // An intermediate that a later norm reads (the tail's h, add_then_norm's s)
-// is normalised as it is stored: rounded to the storage type first (the
-// identity for f32).
+// is stored rounded to the storage type, and the later norm works from its
+// f32 value, so y carries one rounding (normalising the rounded copy would
+// add the rounding of the row's largest element to every output). For f32
+// storage the two are the same.
 //
 // Design (HBM-bound, no contraction, so no MFMA):
 // * Each row is read from HBM exactly once: every lane loads its share of the
@@ -149,7 +151,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
 
     T *out0 = static_cast<T *>(p.out0) + off;
     if constexpr (OP == OP_ADD_NORM) {
-        // s = a + b, rounded to storage, stored, and kept for the norm.
+        // s = a + b: stored rounded to storage, kept in f32 for the norm.
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int i = vbase + k * vstride;
@@ -157,7 +159,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                 float b[W];
                 C::load_nt(x1, i, b);
 #pragma unroll
-                for (int e = 0; e < W; ++e) v0[k][e] = C::round(v0[k][e] + b[e]);
+                for (int e = 0; e < W; ++e) v0[k][e] = v0[k][e] + b[e];
                 C::store_nt(out0, i, v0[k]);
             }
         }
@@ -165,7 +167,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
         for (int q = 0; q < EX; ++q) {
             const int j = sbase + q * sstride;
             if (live && sown && j < rem) {
-                e0[q] = C::round(e0[q] + C::load1_nt(x1, tail0 + j));
+                e0[q] = e0[q] + C::load1_nt(x1, tail0 + j);
                 C::store1_nt(out0, tail0 + j, e0[q]);
             }
         }
@@ -199,8 +201,9 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                 C::store1_nt(y, tail0 + j, e0[q] * inv0 * gain1(0, q, j));
         }
     } else {
-        // h = r + a * inv * gamma0, kept in registers (v1/e1, or v0/e0 once
-        // a is consumed when r is late). norm_then_add stores h * scale.
+        // h = r + a * inv * gamma0, stored rounded and kept in f32 registers
+        // (v1/e1, or v0/e0 once a is consumed when r is late) for the second
+        // norm. norm_then_add stores h * scale.
         const float scale = (OP == OP_NORM_ADD && p.scale) ? *p.scale : 1.0f;
         float(*hv)[W] = LATE ? v0 : v1;
         float *he = LATE ? e0 : e1;
@@ -219,7 +222,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                 if constexpr (OP == OP_TAIL) {
 #pragma unroll
                     for (int e = 0; e < W; ++e)
-                        hv[k][e] = C::round(fmaf(v0[k][e] * inv0, g[e], rr[e]));
+                        hv[k][e] = fmaf(v0[k][e] * inv0, g[e], rr[e]);
                     C::store_nt(out0, i, hv[k]);
                 } else {
                     float o[W];
@@ -237,7 +240,7 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                 const float rr = LATE ? C::load1_nt(x1, tail0 + j) : e1[q];
                 const float h = fmaf(e0[q] * inv0, gain1(0, q, j), rr);
                 if constexpr (OP == OP_TAIL) {
-                    he[q] = C::round(h);
+                    he[q] = h;
                     C::store1_nt(out0, tail0 + j, he[q]);
                 } else {
                     C::store1_nt(out0, tail0 + j, h * scale);
@@ -461,11 +464,15 @@ pass_scale(RowArgs p, const void *src, const void *gain, void *dst,
         [&](int j) { C::store1_nt(y, j, C::load1_nt(x, j) * r * C::load1(g, j)); });
 }
 
-// The elementwise middle pass, with the chunk's sum of squares of what it
-// stores in part[rl * chunks + c] when a later norm needs it:
-//   tail:          h = round(r + a * inv * gamma0)                 (+ part)
+// The elementwise middle pass, with the chunk's sum of squares in
+// part[rl * chunks + c] when a later norm needs it:
+//   tail:          h = r + a * inv * gamma0                        (+ part)
 //   norm_then_add: out = (a * inv * gamma0 + r) * scale
-//   add_then_norm: s = round(a + b)                                (+ part)
+//   add_then_norm: s = a + b                                       (+ part)
+// The sums of squares are of the f32 values; the stored copies are rounded
+// to storage. The last pass reads those stored copies, so in 16-bit storage
+// y = (stored h) * (1/rms of the f32 h) * gain carries two roundings here,
+// against one in the register-resident kernels.
 template <int OP, int ST>
 __global__ void __launch_bounds__(MB)
 pass_fuse(RowArgs p, int64_t row0, int chunks, const float *inv, float *part) {
@@ -483,8 +490,8 @@ pass_fuse(RowArgs p, int64_t row0, int chunks, const float *inv, float *part) {
     const float ia = OP == OP_ADD_NORM ? 0.0f : inv[rl];
     const float scale = (OP == OP_NORM_ADD && p.scale) ? *p.scale : 1.0f;
     auto fuse = [&](float av, float rv, float gv) {
-        if constexpr (OP == OP_ADD_NORM) return C::round(av + rv);
-        else if constexpr (OP == OP_TAIL) return C::round(fmaf(av * ia, gv, rv));
+        if constexpr (OP == OP_ADD_NORM) return av + rv;
+        else if constexpr (OP == OP_TAIL) return fmaf(av * ia, gv, rv);
         else return fmaf(av * ia, gv, rv) * scale;
     };
     float s = 0.0f;

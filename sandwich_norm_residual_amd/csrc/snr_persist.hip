@@ -97,13 +97,13 @@ persist_kernel(RowArgs p, int64_t row0, int64_t row_end) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) dec(x0[k], v0[k]);
         if constexpr (OP == OP_ADD_NORM) {
-            // s = a + b, rounded to storage, stored, and kept for the norm
+            // s = a + b: stored rounded to storage, kept in f32 for the norm
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 float b[W];
                 dec(x1[k], b);
 #pragma unroll
-                for (int e = 0; e < W; ++e) v0[k][e] = C::round(v0[k][e] + b[e]);
+                for (int e = 0; e < W; ++e) v0[k][e] = v0[k][e] + b[e];
                 store(o0, k, v0[k]);
             }
         }
@@ -133,7 +133,7 @@ persist_kernel(RowArgs p, int64_t row0, int64_t row_end) {
                 if constexpr (OP == OP_TAIL) {
 #pragma unroll
                     for (int e = 0; e < W; ++e)
-                        h[k][e] = C::round(fmaf(v0[k][e] * inv0, g[e], rr[e]));
+                        h[k][e] = fmaf(v0[k][e] * inv0, g[e], rr[e]);
                     store(o0, k, h[k]);
                 } else {
                     float o[W];

@@ -16,7 +16,9 @@ reading used throughout):
 Where a denominator is zero the GPU value must equal the oracle's exactly.
 Tolerances: f32 <= 1e-5 (the dormouse report's gate against a scalar f64
 definition); bf16 <= 8e-3 (about two bf16 units 2^-8: one output rounding,
-plus at most one rounding of a stored intermediate that a later norm reads);
+plus, on the multi-pass path only, the rounding of the stored intermediate
+that its last pass re-reads; elsewhere a later norm works from the f32
+intermediate);
 f16 <= 2e-3 (the same budget in f16 units, 4 x 2^-11). For f16 the
 denominator is at least the smallest normal 2^-14: below it f16 holds values
 to an absolute 2^-25, not to a relative 2^-11.
