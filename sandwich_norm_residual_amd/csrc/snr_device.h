@@ -332,8 +332,19 @@ pass_sumsq(RowArgs p, const void *src, int64_t row0, int chunks, float *part) {
 pass_combine(const float *part, int chunks, int n, float eps, float *inv) {
     __shared__ float red[MB / 64];
     const int64_t rl = blockIdx.x;
-    float s = 0.0f;
-    for (int c = threadIdx.x; c < chunks; c += MB) s += part[rl * chunks + c];
+    // each thread adds its chunks (c, c + MB, ...) in blocks of 32, then the
+    // block sums: chains of at most 32 + chunks / (32 MB) additions
+    float s = 0.0f, blk = 0.0f;
+    int cnt = 0;
+    for (int c = threadIdx.x; c < chunks; c += MB) {
+        blk += part[rl * chunks + c];
+        if (++cnt == 32) {
+            s += blk;
+            blk = 0.0f;
+            cnt = 0;
+        }
+    }
+    s += blk;
     const float t = block_total(s, red);
     if (threadIdx.x == 0) inv[rl] = inv_rms(t, n, eps);
 }

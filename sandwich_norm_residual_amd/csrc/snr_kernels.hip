@@ -393,8 +393,17 @@ __device__ float cross_chunk_total(float partial, const SplitState &st,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    float t = part[0];
-    for (int j = 1; j < chunks; ++j) t += part[j];
+    // In chunk order, in blocks of 32: a chain of at most 32 + 31 additions
+    // instead of `chunks` (equal partials, as a constant row gives, drift by
+    // about one rounding per addition in a single chain). Every lane adds in
+    // the same order, so all get the same bits.
+    float t = 0.0f;
+    for (int b = 0; b < chunks; b += 32) {
+        const int e = b + 32 < chunks ? b + 32 : chunks;
+        float s = part[b];
+        for (int j = b + 1; j < e; ++j) s += part[j];
+        t = b == 0 ? s : t + s;
+    }
     return t;
 }
 

@@ -368,6 +368,50 @@ def test_subnormal_epsilon(oracle, n):
     assert not h[1].any() and not y[1].any()
 
 
+@pytest.mark.parametrize("shape,n,op", [("split", 8192 * 1024, "plain"),
+                                        ("split", 700 * 8192, "tail"),
+                                        ("multipass", 8192 * 1024, "plain"),
+                                        ("multipass", 4 * 8192 * 1024 + 5,
+                                         "plain")])
+def test_wide_constant_rows(oracle, shape, n, op):
+    """Constant rows cut into 700 to 1024 chunks (4097 per row on the
+    multi-pass path): every chunk's partial sum of squares is the same,
+    which is where adding the partials in one chain drifts by about a
+    rounding per addition (1e-5 of the sum at 1024 chunks). Added in blocks
+    of 32 they stay within 2e-6 of the exact result."""
+    say(f"wide constant rows {shape} {op} n={n}")
+    rows = 2
+    if op == "plain":
+        x = np.empty((rows, n), np.float32)
+        x[0], x[1] = np.float32(0.7), np.float32(-1.1)
+        g = np.full(n, np.float32(1.3))
+        inp = {"x": x, "gamma": g, "eps": 1e-5, "dtype": "f32"}
+        with snr.forced_shape(shape, 0, 8):
+            got, _ = run_plain(inp)
+            sh = snr.last_shape()
+        want = oracle.rmsnorm(x, g, 1e-5)
+        from parity import plain_error
+        err = plain_error(got, want)
+    else:
+        a = np.empty((rows, n), np.float32)
+        r = np.empty((rows, n), np.float32)
+        a[0], a[1] = np.float32(0.3), np.float32(2.5)
+        r[0], r[1] = np.float32(-0.9), np.float32(0.1)
+        gp, gq = np.full(n, np.float32(1.1)), np.full(n, np.float32(0.7))
+        inp = {"a": a, "r": r, "gamma_post": gp, "gamma_pre": gq,
+               "eps_post": 1e-8, "eps_pre": 1e-5, "dtype": "f32"}
+        with snr.forced_shape(shape, 0, 8):
+            h, y = run_tail(inp)
+            sh = snr.last_shape()
+        from parity import tail_errors
+        o = oracle.sandwich_tail(a, r, gp, 1e-8, gq, 1e-5)
+        err = max(tail_errors(h, y, o, r, gq))
+    say(f"  {sh}: max rel err {err:.3e}")
+    assert sh.startswith(shape + ":"), sh
+    assert err < 2e-6, err
+    assert snr.split_timeouts() == 0
+
+
 def test_rows_zero_is_a_noop():
     say("rows=0")
     x = torch.empty(0, 64, device=DEV)
