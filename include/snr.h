@@ -85,9 +85,13 @@ enum {
  *
  *   x      [rows, n] input, dtype `dtype`, device memory
  *   gamma  [n] per-channel gain, same dtype as x
- *   eps    epsilon added to the mean of squares; finite and > 0 (a
- *          subnormal epsilon is computed; one so large that the mean of
- *          squares plus epsilon overflows f32 gives 1/rms = 0)
+ *   eps    epsilon added to the mean of squares; finite and > 0.
+ *          Sums of squares are f32: a row's n * mean(x^2) must stay below
+ *          3.4e38, and mean(x^2) + eps too (else 1/rms = 0). A subnormal
+ *          epsilon is computed, but squares below 2^-126 lose precision and
+ *          below 2^-150 vanish, so with such an epsilon rows whose mean
+ *          square is itself below about 1e-37 are not accurate; any normal
+ *          epsilon outweighs what those squares lose.
  *   rows   number of rows (>= 0)
  *   n      row width (>= 1)
  *   dtype  SNR_F32, SNR_BF16 or SNR_F16 (storage of x, gamma and y)
