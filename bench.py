@@ -9,7 +9,10 @@ eps_pre = 1e-5). A step is one sandwich_tail call over the whole batch.
 Prints ONE JSON line on stdout: achieved HBM GB/s from algorithmic bytes
 (row streams plus each gain once per launch) over wall time, rows/s, the
 dominant kernel's roofline (per-launch time from HIP events on the launch
-stream) and the f64 oracle's throughput on the host cores.
+stream; HBM traffic from the committed byte-counter summary), the attainable
+floor on the same GPU (plain read, write and copy kernels of
+bench_stream.hip, and the step's own row access pattern with no
+arithmetic), and the f64 oracle's throughput on the host cores.
 
 Inputs are resident in HBM before timing starts. Rotating sets of
 input/output buffers (at least three, and together at least 1 GiB of step
