@@ -61,8 +61,9 @@ namespace {
 // LATE (tail and norm_then_add): r is loaded while forming the output
 // instead of together with a, so only one row stream is held in registers.
 // add_then_norm always holds only the sum s = a + b.
+// EARLY: the gains are loaded with the row (see below).
 // ---------------------------------------------------------------------------
-template <int OP, int ST, int VPT, int EX, bool LATE, class Reduce>
+template <int OP, int ST, int VPT, int EX, bool LATE, bool EARLY, class Reduce>
 __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                                             bool live, int vbase, int vstride,
                                             int sbase, int sstride, bool sown,
@@ -106,16 +107,18 @@ __device__ __forceinline__ void process_row(const RowArgs &p, int64_t off,
                                               : 0.0f;
         }
     }
-    // Gains are loaded one vector just before its use, except that
-    // norm_then_add loads its gain with the row (PRE) where registers allow:
-    // measured 53.5 -> 52.6 us at 4096 x 6656 f32. The vector memory counter
-    // retires in issue order and counts stores too, so a gain loaded between
-    // two stores is waited for together with the first store; the tail, the
-    // plain norm and add_then_norm measured no faster without those waits
-    // (the tail 71.4 -> 74.7 us with its gains loaded with the row), so they
-    // keep the late loads.
+    // Gains are loaded one vector just before its use, or with the row (PRE)
+    // where registers allow: always for norm_then_add (measured 53.5 ->
+    // 52.6 us at 4096 x 6656 f32), and for the other operations when the
+    // launch asks for it (EARLY). The vector memory counter retires in issue
+    // order and counts stores too, so a gain loaded between two stores is
+    // waited for together with the first store. For a few rows the step is
+    // one memory round trip after another and loading the gains with the
+    // row takes one of them away (1 row x 6656 f32: tail 3.38 -> 3.24 us,
+    // plain 2.36 -> 2.26 us); over many rows the late loads measured faster
+    // (4096 rows: tail 73.0 -> 75.7 us with the gains loaded with the row).
     using V = typename C::vec;
-    constexpr bool PRE = OP == OP_NORM_ADD && !LATE && VPT <= 4;
+    constexpr bool PRE = (OP == OP_NORM_ADD || EARLY) && !LATE && VPT <= 4;
     constexpr int NG = OP == OP_TAIL ? 2 : 1;
     const T *gp[2] = {static_cast<const T *>(p.g0),
                       static_cast<const T *>(OP == OP_TAIL ? p.g1 : p.g0)};
@@ -295,7 +298,16 @@ constexpr bool rowtile_late() {
            VPT * Codec<ST>::W >= 64;
 }
 
+// The row tiles that also have a form with the gains loaded with the row:
+// one row per workgroup, a register tile that leaves room for the gains, and
+// an operation that does not load them with the row already.
 template <int OP, int ST, int G, int VPT>
+constexpr bool rowtile_has_early() {
+    return OP != OP_NORM_ADD && G >= 64 && VPT <= 4 &&
+           !rowtile_late<OP, ST, G, VPT>();
+}
+
+template <int OP, int ST, int G, int VPT, bool EARLY>
 __global__ void __launch_bounds__(rowtile_block<G>())
 rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     constexpr int BLOCK = rowtile_block<G>();
@@ -308,7 +320,7 @@ rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     const bool live = row < row_end;
     const int64_t off = live ? row * (int64_t)p.n : 0;
     process_row<OP, ST, VPT, rowtile_extra<ST, G>(),
-                rowtile_late<OP, ST, G, VPT>()>(
+                rowtile_late<OP, ST, G, VPT>(), EARLY>(
         p, off, live, sub, G, sub, G, true,
         [&](float s, int which) { return row_total<G>(s, red[which]); });
 }
@@ -338,7 +350,7 @@ multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
     p.nv = m.nv;
     p.rem = m.rem;
     const int64_t off = live ? (row - m.row_start[seg]) * (int64_t)m.n : 0;
-    process_row<OP_PLAIN, ST, VPT, rowtile_extra<ST, G>(), false>(
+    process_row<OP_PLAIN, ST, VPT, rowtile_extra<ST, G>(), false, false>(
         p, off, live, sub, G, sub, G, true,
         [&](float s, int which) { return row_total<G>(s, red[which]); });
 }
@@ -422,7 +434,7 @@ split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
 
     for (int64_t rl = group; rl < nrows; rl += groups) {
         const int64_t off = (row0 + rl) * (int64_t)p.n;
-        process_row<OP, ST, VPT, 1, false>(
+        process_row<OP, ST, VPT, 1, false, false>(
             p, off, true, vbase, SB, tid, SB, last,
             [&](float s, int which) {
                 return cross_chunk_total(block_total(s, red[which]), st, which,
@@ -539,22 +551,36 @@ __global__ void zero_kernel(unsigned int *p, int64_t words) {
 // ---------------------------------------------------------------------------
 // Launchers and the kernel table
 // ---------------------------------------------------------------------------
+// Launches of at most kEarlyRows rows use the form with the gains loaded
+// with the row where there is one. Measured over 1 to 256 rows of 6656 f32
+// (steps replayed from a HIP graph): faster for every operation up to 16
+// rows (the tail 3.60 -> 3.47 us at 16 rows), even at 32 (4.16 -> 4.10 us
+// in one run, 4.04 -> 4.11 us in another), slower for the tail and the plain
+// norm from 64 rows on (4.55 -> 4.81 us, 3.17 -> 3.27 us).
 template <int OP, int ST, int G, int VPT>
 hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
                           hipStream_t stream) {
     constexpr int BLOCK = rowtile_block<G>();
     constexpr int RPB = BLOCK / G;
     const int64_t blocks = (nrows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT>),
-                       dim3((unsigned int)blocks), dim3(BLOCK), 0, stream, p,
-                       row0, row0 + nrows);
+    const dim3 grid((unsigned int)blocks);
+    if constexpr (rowtile_has_early<OP, ST, G, VPT>()) {
+        if (nrows <= kEarlyRows) {
+            hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT, true>), grid,
+                               dim3(BLOCK), 0, stream, p, row0, row0 + nrows);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT, false>), grid,
+                       dim3(BLOCK), 0, stream, p, row0, row0 + nrows);
     return hipGetLastError();
 }
 
 template <int OP, int ST, int G, int VPT>
 hipError_t occupancy_rowtile(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, rowtile_kernel<OP, ST, G, VPT>, rowtile_block<G>(), 0);
+        blocks_per_cu, rowtile_kernel<OP, ST, G, VPT, false>,
+        rowtile_block<G>(), 0);
 }
 
 template <int ST, int G, int VPT>
