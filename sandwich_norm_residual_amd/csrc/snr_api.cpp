@@ -187,7 +187,10 @@ int split_chunks(const KernelEntry *k, int64_t nv) {
     return (int)(c > 0 ? c : 1);  // a row of only remainder elements
 }
 
-int choose(int op, int st, int w, int64_t nv, int rem, Choice *c) {
+// `rows` is the launch's row count (0 where the caller needs a row tile:
+// the several-segment launch).
+int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
+           Choice *c) {
     if (t_force_kind == SNR_SHAPE_PERSIST) {
         if (op == OP_NORM_Q8 || rem != 0) return SNR_ERR_SHAPE;
         c->k = find_entry(op, st, w, KIND_PERSIST, t_force_g, t_force_vpt);
@@ -258,11 +261,17 @@ int choose(int op, int st, int w, int64_t nv, int rem, Choice *c) {
     // The persistent form of the same tile (loads of the next row in flight
     // through this row's reductions) measured faster for the 16-bit tail
     // and its halves with 512 or more lanes per row (4096 x 6656: bf16 tail
-    // 43.1 -> 40.9 us, norm_then_add 32.4 -> 30.0 us) and slower for f32,
-    // for the plain norm and for smaller groups, whose rows are shorter than
-    // the loop's fixed cost; it needs rows without a ragged end.
-    if (st != ST_F32 && rem == 0 && best->g >= 512 &&
-        (op == OP_TAIL || op == OP_NORM_ADD || op == OP_ADD_NORM)) {
+    // 43.1 -> 40.9 us, norm_then_add 32.4 -> 30.0 us), and for the 16-bit
+    // plain norm with 1024 lanes per row over 256 rows or more (n = 16384
+    // bf16: 1024 rows 14.6 -> 12.5 us, 8192 rows 93.8 -> 88.7 us). It
+    // measured slower or no faster for f32, for the plain norm with 512
+    // lanes (slower at 1024 and 16384 rows of 6656 bf16, faster between),
+    // for few rows of the plain norm and for smaller groups, whose rows are
+    // shorter than the loop's fixed cost; it needs rows without a ragged
+    // end.
+    const bool halves = op == OP_TAIL || op == OP_NORM_ADD || op == OP_ADD_NORM;
+    const bool wide_plain = op == OP_PLAIN && best->g == 1024 && rows >= 256;
+    if (st != ST_F32 && rem == 0 && best->g >= 512 && (halves || wide_plain)) {
         const KernelEntry *pk =
             find_entry(op, st, w, KIND_PERSIST, best->g, best->vpt);
         if (pk) c->k = pk;
@@ -287,7 +296,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     a.nv = (int32_t)(a.n / w);
     a.rem = (int32_t)(a.n % w);
     Choice c;
-    rc = choose(op, st, w, a.nv, a.rem, &c);
+    rc = choose(op, st, w, a.nv, a.rem, a.rows, &c);
     if (rc != SNR_OK) return rc;
     const KernelEntry *k = c.k;
 
@@ -616,7 +625,7 @@ int rmsnorm_fwd_multi(const snr_segment *segs, int count, int64_t n,
     if (rc != SNR_OK) return rc;
     const int w = (int)(16 / es);
     Choice c;
-    rc = choose(OP_PLAIN, st, w, n / w, (int)(n % w), &c);
+    rc = choose(OP_PLAIN, st, w, n / w, (int)(n % w), 0, &c);
     if (rc != SNR_OK) return rc;
     if (c.k->kind != KIND_ROWTILE || !c.k->multi) {
         // rows too wide for one register tile (or a forced shape without a

@@ -108,3 +108,31 @@ def test_persist_rejects_ragged_rows():
     with snr.forced_shape("persist", 128, 2):
         with pytest.raises(snr.SnrError):
             run_plain(inp)
+
+
+@pytest.mark.parametrize("case", [("bf16", 16384, 256, "persist:1024:2:8"),
+                                  ("f16", 12288, 1000, "persist:1024:2:8"),
+                                  ("bf16", 16384, 255, "rowtile:1024:2:8"),
+                                  ("bf16", 16379, 300, "rowtile:1024:2:8"),
+                                  ("bf16", 6656, 4096, "rowtile:512:2:8"),
+                                  ("f32", 6656, 4096, "rowtile:1024:2:4")],
+                         ids=lambda c: "{}-n{}-rows{}".format(*c[:3]))
+def test_automatic_plain_persist_choice(oracle, case):
+    """The plain norm takes the persistent tile automatically only in 16-bit
+    storage, with 1024 lanes per row, rows without a ragged end and 256 rows
+    or more; the result is bit-equal to the forced row tile and matches the
+    oracle on sampled rows."""
+    st, n, rows, want = case
+    label = f"auto-plain-{st}-n{n}-rows{rows}"
+    say(label)
+    inp = _inputs("plain", st, rows, n, 35000 + rows + n)
+    got = _run("plain", inp)
+    assert snr.last_shape() == want, (label, snr.last_shape())
+    _, g, v, _w = want.split(":")
+    with snr.forced_shape("rowtile", int(g), int(v)):
+        ref = _run("plain", inp)
+    assert np.array_equal(got[0].view(np.uint8), ref[0].view(np.uint8)), label
+    pick = np.r_[0:3, rows // 2:rows // 2 + 3, rows - 3:rows]
+    sub = {k: (val[pick] if isinstance(val, np.ndarray) and val.ndim == 2
+               else val) for k, val in inp.items()}
+    _check(oracle, "plain", sub, [got[0][pick]], label + "-sampled")
