@@ -73,9 +73,9 @@ struct SplitState {
     uint32_t spin_limit;        // polls before a wait gives up
 };
 
-// Row-tile launches of at most this many rows load the gains with the row
-// (one memory round trip fewer per step; slower over many rows).
-constexpr int64_t kEarlyRows = 16;
+// Row-tile launches of at most this many workgroups load the gains with the
+// row (one memory round trip fewer per step; slower over many rows).
+constexpr int64_t kEarlyBlocks = 16;
 
 // Chunk geometry of the split-row kernels: 256 threads per workgroup, each
 // holding `vpt` loads of the chunk.

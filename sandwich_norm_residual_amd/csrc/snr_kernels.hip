@@ -299,12 +299,11 @@ constexpr bool rowtile_late() {
 }
 
 // The row tiles that also have a form with the gains loaded with the row:
-// one row per workgroup, a register tile that leaves room for the gains, and
-// an operation that does not load them with the row already.
+// a register tile that leaves room for the gains, and an operation that does
+// not load them with the row already.
 template <int OP, int ST, int G, int VPT>
 constexpr bool rowtile_has_early() {
-    return OP != OP_NORM_ADD && G >= 64 && VPT <= 4 &&
-           !rowtile_late<OP, ST, G, VPT>();
+    return OP != OP_NORM_ADD && VPT <= 4 && !rowtile_late<OP, ST, G, VPT>();
 }
 
 template <int OP, int ST, int G, int VPT, bool EARLY>
@@ -328,7 +327,7 @@ rowtile_kernel(RowArgs p, int64_t row0, int64_t row_end) {
 // Several RMSNorms in one launch (the same row tile as above): each row
 // finds its segment in the table and normalises with that segment's
 // tensors and epsilon.
-template <int ST, int G, int VPT>
+template <int ST, int G, int VPT, bool EARLY>
 __global__ void __launch_bounds__(rowtile_block<G>())
 multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
     constexpr int BLOCK = rowtile_block<G>();
@@ -350,7 +349,7 @@ multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
     p.nv = m.nv;
     p.rem = m.rem;
     const int64_t off = live ? (row - m.row_start[seg]) * (int64_t)m.n : 0;
-    process_row<OP_PLAIN, ST, VPT, rowtile_extra<ST, G>(), false, false>(
+    process_row<OP_PLAIN, ST, VPT, rowtile_extra<ST, G>(), false, EARLY>(
         p, off, live, sub, G, sub, G, true,
         [&](float s, int which) { return row_total<G>(s, red[which]); });
 }
@@ -551,12 +550,16 @@ __global__ void zero_kernel(unsigned int *p, int64_t words) {
 // ---------------------------------------------------------------------------
 // Launchers and the kernel table
 // ---------------------------------------------------------------------------
-// Launches of at most kEarlyRows rows use the form with the gains loaded
-// with the row where there is one. Measured over 1 to 256 rows of 6656 f32
-// (steps replayed from a HIP graph): faster for every operation up to 16
-// rows (the tail 3.60 -> 3.47 us at 16 rows), even at 32 (4.16 -> 4.10 us
-// in one run, 4.04 -> 4.11 us in another), slower for the tail and the plain
-// norm from 64 rows on (4.55 -> 4.81 us, 3.17 -> 3.27 us).
+// Launches of at most kEarlyBlocks workgroups use the form with the gains
+// loaded with the row where there is one. Measured over 1 to 256 rows of
+// 6656 f32 (one row per workgroup; steps replayed from a HIP graph): faster
+// for every operation up to 16 rows (the tail 3.60 -> 3.47 us at 16 rows),
+// even at 32 (4.16 -> 4.10 us in one run, 4.04 -> 4.11 us in another),
+// slower for the tail and the plain norm from 64 rows on (4.55 -> 4.81 us,
+// 3.17 -> 3.27 us). With several rows per workgroup the count that matters
+// is the same: the per-head query and key norms of one token (52 + 8 rows
+// of 128 f32, two workgroups) took 2.60 -> 2.26 us in one several-segment
+// launch and 4.19 -> 3.55 us in two launches.
 template <int OP, int ST, int G, int VPT>
 hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
                           hipStream_t stream) {
@@ -565,7 +568,7 @@ hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
     const int64_t blocks = (nrows + RPB - 1) / RPB;
     const dim3 grid((unsigned int)blocks);
     if constexpr (rowtile_has_early<OP, ST, G, VPT>()) {
-        if (nrows <= kEarlyRows) {
+        if (blocks <= kEarlyBlocks) {
             hipLaunchKernelGGL((rowtile_kernel<OP, ST, G, VPT, true>), grid,
                                dim3(BLOCK), 0, stream, p, row0, row0 + nrows);
             return hipGetLastError();
@@ -589,8 +592,16 @@ hipError_t launch_multi(const MultiArgs &m, int64_t row0, int64_t nrows,
     constexpr int BLOCK = rowtile_block<G>();
     constexpr int RPB = BLOCK / G;
     const int64_t blocks = (nrows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((multi_kernel<ST, G, VPT>), dim3((unsigned int)blocks),
-                       dim3(BLOCK), 0, stream, m, row0, row0 + nrows);
+    const dim3 grid((unsigned int)blocks);
+    if constexpr (rowtile_has_early<OP_PLAIN, ST, G, VPT>()) {
+        if (blocks <= kEarlyBlocks) {
+            hipLaunchKernelGGL((multi_kernel<ST, G, VPT, true>), grid,
+                               dim3(BLOCK), 0, stream, m, row0, row0 + nrows);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((multi_kernel<ST, G, VPT, false>), grid, dim3(BLOCK), 0,
+                       stream, m, row0, row0 + nrows);
     return hipGetLastError();
 }
 

@@ -1,15 +1,17 @@
-"""Row-tile launches of at most 16 rows load the gains together with the row;
-longer launches load each gain vector just before its use. Only the time a
-load is issued differs, not the arithmetic, so the two forms must agree bit
-for bit.
+"""Row-tile launches of at most 16 workgroups load the gains together with
+the row; larger launches load each gain vector just before its use. Only the
+time a load is issued differs, not the arithmetic, so the two forms must
+agree bit for bit.
 
-For each row tile that has both forms (one row per workgroup, at most four
-vectors per lane), forced, with a ragged row that fills the tile: 40 rows in
-one launch (gains loaded late) against the same rows in launches of 16, 7
-and 1 rows (gains loaded with the row) and of the 16 rows left (late again)
-on slices of the same buffers. Every slice must equal the matching rows of
-the 40-row launch, and the 16-row launch is also checked against the
-oracle."""
+For each row tile that has both forms (at most four vectors per lane;
+sub-wavefront tiles included, whose 256-lane workgroups hold 256 / G rows),
+forced, with a ragged row that fills the tile: 26 workgroups' worth of rows
+in one launch (gains loaded late) against the same rows in launches of 16
+workgroups, 7 rows, 1 row and the rest (gains loaded with the row) on slices
+of the same buffers. Every slice must equal the matching rows of the whole
+launch, and the first slice is also checked against the oracle. The
+several-segment launch is checked the same way: two segments in one launch
+of 52 workgroups against their first rows in a launch of 16."""
 import numpy as np
 import pytest
 
@@ -22,16 +24,29 @@ from gpu_helpers import (check_add_norm, check_plain, check_tail, dev,  # noqa: 
 
 pytestmark = pytest.mark.gpu
 
-ROWS = 40
-PIECES = ((0, 16), (16, 23), (23, 24), (24, 40))   # 16, 7, 1, 16 rows
-TILES = ((128, 2), (256, 2), (256, 4), (512, 2), (512, 4), (1024, 1),
-         (1024, 2), (1024, 4))
+EARLY_BLOCKS = 16
+TILES = ((1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (32, 4), (128, 2),
+         (256, 2), (256, 4), (512, 2), (512, 4), (1024, 1), (1024, 2),
+         (1024, 4))
 WIDTH = {"f32": 4, "bf16": 8, "f16": 8}
+BITS = {"f32": torch.int32, "bf16": torch.int16, "f16": torch.int16}
 
 CASES = [(op, dtype, g, vpt)
          for op in ("plain", "tail", "add_norm")
          for dtype in ("f32", "bf16", "f16")
          for g, vpt in TILES]
+MULTI_CASES = [(dtype, g, vpt) for dtype in ("f32", "bf16")
+               for g, vpt in TILES]
+
+
+def _rows_per_block(g):
+    return 256 // g if g < 128 else 1
+
+
+def _pieces(rpb):
+    """Row ranges: 16 workgroups, 7 rows, 1 row, the rest (all early)."""
+    a = EARLY_BLOCKS * rpb
+    return ((0, a), (a, a + 7), (a + 7, a + 8), (a + 8, 26 * rpb))
 
 
 def _gain(rng, n, dtype):
@@ -39,8 +54,8 @@ def _gain(rng, n, dtype):
                           .astype(np.float32), dtype)
 
 
-def _rows(rng, n, dtype, scale=1.0):
-    return gen.to_storage((scale * rng.standard_normal((ROWS, n)))
+def _rows(rng, rows, n, dtype, scale=1.0):
+    return gen.to_storage((scale * rng.standard_normal((rows, n)))
                           .astype(np.float32), dtype)
 
 
@@ -58,22 +73,29 @@ def _call(op, ins, outs, lo, hi, eps):
                           y_out=ol[1])
 
 
+def _same_bits(a, b, dtype):
+    return torch.equal(a.view(BITS[dtype]), b.view(BITS[dtype]))
+
+
 @pytest.mark.parametrize("case", CASES,
                          ids=["-".join(map(str, c)) for c in CASES])
 def test_early_and_late_gains_agree(oracle, case):
     op, dtype, g, vpt = case
+    rpb = _rows_per_block(g)
+    rows = 26 * rpb
     n = g * vpt * WIDTH[dtype] - 3        # the tile's last vector ragged
-    label = f"early-gains {op} {dtype} rowtile {g}x{vpt} n={n}"
+    label = f"early-gains {op} {dtype} rowtile {g}x{vpt} n={n} rows={rows}"
     say(label)
     rng = gen.rng_for(60000 + 31 * g + vpt + 7 * n)
     if op == "plain":
-        inp = {"x": _rows(rng, n, dtype), "gamma": _gain(rng, n, dtype),
-               "eps": 1e-5, "dtype": dtype}
+        inp = {"x": _rows(rng, rows, n, dtype),
+               "gamma": _gain(rng, n, dtype), "eps": 1e-5, "dtype": dtype}
         ins = [dev(inp["x"], dtype)]
         eps = (inp["eps"],)
         keys = ("gamma",)
     elif op == "tail":
-        inp = {"a": _rows(rng, n, dtype), "r": _rows(rng, n, dtype, 3.0),
+        inp = {"a": _rows(rng, rows, n, dtype),
+               "r": _rows(rng, rows, n, dtype, 3.0),
                "gamma_post": _gain(rng, n, dtype),
                "gamma_pre": _gain(rng, n, dtype), "eps_post": 1e-8,
                "eps_pre": 1e-5, "dtype": dtype}
@@ -81,7 +103,8 @@ def test_early_and_late_gains_agree(oracle, case):
         eps = (inp["eps_post"], inp["eps_pre"])
         keys = ("gamma_post", "gamma_pre")
     else:
-        inp = {"a": _rows(rng, n, dtype), "b": _rows(rng, n, dtype, 0.5),
+        inp = {"a": _rows(rng, rows, n, dtype),
+               "b": _rows(rng, rows, n, dtype, 0.5),
                "gamma": _gain(rng, n, dtype), "eps": 1e-5, "dtype": dtype}
         ins = [dev(inp["a"], dtype), dev(inp["b"], dtype)]
         eps = (inp["eps"],)
@@ -90,21 +113,19 @@ def test_early_and_late_gains_agree(oracle, case):
     outs_n = 1 if op == "plain" else 2
     whole = [torch.full_like(ins[0], float("nan")) for _ in range(outs_n)]
     parts = [torch.full_like(ins[0], float("nan")) for _ in range(outs_n)]
+    pieces = _pieces(rpb)
     with snr.forced_shape("rowtile", g, vpt):
-        _call(op, ins, whole, 0, ROWS, eps)
+        _call(op, ins, whole, 0, rows, eps)
         assert snr.last_shape() == f"rowtile:{g}:{vpt}:{WIDTH[dtype]}", \
             snr.last_shape()
-        for lo, hi in PIECES:
+        for lo, hi in pieces:
             _call(op, ins, parts, lo, hi, eps)
     torch.cuda.synchronize()
     for w, p in zip(whole, parts):
-        assert torch.equal(w.view(torch.int16 if dtype != "f32"
-                                  else torch.int32),
-                           p.view(torch.int16 if dtype != "f32"
-                                  else torch.int32)), label
+        assert _same_bits(w, p, dtype), label
 
-    # the first 16-row launch against the oracle
-    lo, hi = PIECES[0]
+    # the first slice against the oracle
+    lo, hi = pieces[0]
     sub = {k: (v[lo:hi] if isinstance(v, np.ndarray) and v.ndim == 2 else v)
            for k, v in inp.items()}
     got = [host_f64(p[lo:hi]) for p in parts]
@@ -114,3 +135,35 @@ def test_early_and_late_gains_agree(oracle, case):
         check_tail(oracle, sub, got[0], got[1], label)
     else:
         check_add_norm(oracle, sub, got[0], got[1], label)
+
+
+@pytest.mark.parametrize("case", MULTI_CASES,
+                         ids=["-".join(map(str, c)) for c in MULTI_CASES])
+def test_multi_early_and_late_gains_agree(oracle, case):
+    dtype, g, vpt = case
+    rpb = _rows_per_block(g)
+    rows = 26 * rpb                        # two segments: 52 workgroups
+    few = 8 * rpb                          # 8 + 8 = 16 workgroups
+    n = g * vpt * WIDTH[dtype] - 3
+    label = f"early-gains multi {dtype} rowtile {g}x{vpt} n={n}"
+    say(label)
+    rng = gen.rng_for(61000 + 31 * g + vpt + 7 * n)
+    xs = [_rows(rng, rows, n, dtype, s) for s in (1.0, 4.0)]
+    gs = [_gain(rng, n, dtype) for _ in range(2)]
+    epss = (1e-5, 1e-6)
+    dx = [dev(x, dtype) for x in xs]
+    dg = [dev(gm, dtype) for gm in gs]
+    whole = [torch.full_like(x, float("nan")) for x in dx]
+    part = [torch.full_like(x[:few], float("nan")) for x in dx]
+    with snr.forced_shape("rowtile", g, vpt):
+        snr.rmsnorm_fwd_multi(list(zip(dx, dg, epss)), whole)
+        assert snr.last_shape().startswith(f"multi:{g}:{vpt}:"), \
+            snr.last_shape()
+        snr.rmsnorm_fwd_multi([(x[:few], gm, e)
+                               for x, gm, e in zip(dx, dg, epss)], part)
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert _same_bits(whole[s][:few], part[s], dtype), (label, s)
+        inp = {"x": xs[s][:few], "gamma": gs[s], "eps": epss[s],
+               "dtype": dtype}
+        check_plain(oracle, inp, host_f64(part[s]), f"{label}-seg{s}")
