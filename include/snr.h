@@ -268,7 +268,10 @@ SNR_API int snr_last_hip_error(void);
  *                             each lane holding `vpt` loads of the row in
  *                             registers; g <= 64 packs several rows in one
  *                             wavefront, g > 64 spans g/64 wavefronts joined
- *                             by one LDS step
+ *                             by one LDS step. A launch of at most 16
+ *                             workgroups loads the gains together with the
+ *                             row (one memory round trip fewer; the same
+ *                             results bit for bit)
  *          SNR_SHAPE_SPLIT    the row is cut into chunks of 256 x `vpt`
  *                             vectors, one workgroup per chunk, joined by a
  *                             two-phase cross-workgroup reduction; every
