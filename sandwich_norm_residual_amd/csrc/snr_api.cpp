@@ -259,19 +259,30 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
     }
     c->k = best;
     // The persistent form of the same tile (loads of the next row in flight
-    // through this row's reductions) measured faster for the 16-bit tail
-    // and its halves with 512 or more lanes per row (4096 x 6656: bf16 tail
-    // 43.1 -> 40.9 us, norm_then_add 32.4 -> 30.0 us), and for the 16-bit
-    // plain norm with 1024 lanes per row over 256 rows or more (n = 16384
-    // bf16: 1024 rows 14.6 -> 12.5 us, 8192 rows 93.8 -> 88.7 us). It
-    // measured slower or no faster for f32, for the plain norm with 512
-    // lanes (slower at 1024 and 16384 rows of 6656 bf16, faster between),
-    // for few rows of the plain norm and for smaller groups, whose rows are
-    // shorter than the loop's fixed cost; it needs rows without a ragged
+    // through this row's reductions) measured faster for:
+    // * the 16-bit tail and its halves with 512 or more lanes per row
+    //   (4096 x 6656: bf16 tail 43.1 -> 40.9 us, norm_then_add 32.4 -> 30.0);
+    // * the 16-bit plain norm with 1024 lanes per row over 256 rows or more
+    //   (n = 16384 bf16: 1024 rows 14.6 -> 12.5 us, 8192 rows 93.8 -> 88.7;
+    //   n = 24576: 1024 rows 19.2 -> 17.7 us);
+    // * the f32 plain norm at 1024 x 4 over 1024 rows or more (n = 16384:
+    //   1024 rows 24.9 -> 22.1 us, 4096 rows 93.9 -> 85.3), and at 1024 x 2
+    //   when the row fills the tile (n = 8192: 1024 rows 13.7 -> 12.9 us,
+    //   16384 rows 186.4 -> 181.1).
+    // It measured slower or no faster for the f32 tail and its halves, for
+    // the f32 plain norm with fewer rows (256 x 16384: 6.97 -> 7.30 us) or
+    // a partly filled 1024 x 2 tile (n = 6656 and 7168: within 1.5% either
+    // way), for the plain norm with 512 lanes (slower at 1024 and 16384 rows
+    // of 6656 bf16, faster between), and for smaller groups, whose rows are
+    // shorter than the loop's fixed cost. It needs rows without a ragged
     // end.
-    const bool halves = op == OP_TAIL || op == OP_NORM_ADD || op == OP_ADD_NORM;
-    const bool wide_plain = op == OP_PLAIN && best->g == 1024 && rows >= 256;
-    if (st != ST_F32 && rem == 0 && best->g >= 512 && (halves || wide_plain)) {
+    const bool halves = st != ST_F32 && best->g >= 512 &&
+                        (op == OP_TAIL || op == OP_NORM_ADD || op == OP_ADD_NORM);
+    const bool f32_tile = best->vpt == 4 || (best->vpt == 2 && nv == 2048);
+    const bool wide_plain =
+        op == OP_PLAIN && best->g == 1024 &&
+        (st != ST_F32 ? rows >= 256 : f32_tile && rows >= 1024);
+    if (rem == 0 && (halves || wide_plain)) {
         const KernelEntry *pk =
             find_entry(op, st, w, KIND_PERSIST, best->g, best->vpt);
         if (pk) c->k = pk;

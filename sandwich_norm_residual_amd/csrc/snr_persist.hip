@@ -206,9 +206,14 @@ hipError_t launch_persist(const RowArgs &p, int64_t row0, int64_t nrows,
     SNR_PERSIST(OP, ST, 512, 2), SNR_PERSIST(OP, ST, 1024, 1),               \
     SNR_PERSIST(OP, ST, 1024, 2)
 
+// 1024 x 4 only for the plain norm: one input stream double-buffered and
+// one gain fit a 1024-lane workgroup's registers; the tail's two streams and
+// two gains would not.
 const KernelEntry kPersistTable[] = {
-    SNR_PERSIST_SHAPES(OP_PLAIN, ST_F32),    SNR_PERSIST_SHAPES(OP_PLAIN, ST_BF16),
-    SNR_PERSIST_SHAPES(OP_PLAIN, ST_F16),    SNR_PERSIST_SHAPES(OP_TAIL, ST_F32),
+    SNR_PERSIST_SHAPES(OP_PLAIN, ST_F32),    SNR_PERSIST(OP_PLAIN, ST_F32, 1024, 4),
+    SNR_PERSIST_SHAPES(OP_PLAIN, ST_BF16),   SNR_PERSIST(OP_PLAIN, ST_BF16, 1024, 4),
+    SNR_PERSIST_SHAPES(OP_PLAIN, ST_F16),    SNR_PERSIST(OP_PLAIN, ST_F16, 1024, 4),
+    SNR_PERSIST_SHAPES(OP_TAIL, ST_F32),
     SNR_PERSIST_SHAPES(OP_TAIL, ST_BF16),    SNR_PERSIST_SHAPES(OP_TAIL, ST_F16),
     SNR_PERSIST_SHAPES(OP_NORM_ADD, ST_F32), SNR_PERSIST_SHAPES(OP_NORM_ADD, ST_BF16),
     SNR_PERSIST_SHAPES(OP_NORM_ADD, ST_F16), SNR_PERSIST_SHAPES(OP_ADD_NORM, ST_F32),

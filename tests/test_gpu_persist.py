@@ -51,8 +51,10 @@ def _check(oracle, op, inp, outs, label):
 
 
 def _cases():
-    return [(op, st, g, v) for op in OPS for st in ("f32", "bf16", "f16")
-            for g, v in SHAPES]
+    # 1024 x 4 is compiled for the plain norm only
+    return ([(op, st, g, v) for op in OPS for st in ("f32", "bf16", "f16")
+             for g, v in SHAPES] +
+            [("plain", st, 1024, 4) for st in ("f32", "bf16", "f16")])
 
 
 @pytest.mark.parametrize("case", _cases(),
@@ -115,13 +117,21 @@ def test_persist_rejects_ragged_rows():
                                   ("bf16", 16384, 255, "rowtile:1024:2:8"),
                                   ("bf16", 16379, 300, "rowtile:1024:2:8"),
                                   ("bf16", 6656, 4096, "rowtile:512:2:8"),
+                                  ("bf16", 24576, 256, "persist:1024:4:8"),
+                                  ("f32", 16384, 1024, "persist:1024:4:4"),
+                                  ("f32", 12288, 1023, "rowtile:1024:4:4"),
+                                  ("f32", 16381, 2048, "rowtile:1024:4:4"),
+                                  ("f32", 8192, 1024, "persist:1024:2:4"),
+                                  ("f32", 8184, 1024, "rowtile:1024:2:4"),
                                   ("f32", 6656, 4096, "rowtile:1024:2:4")],
                          ids=lambda c: "{}-n{}-rows{}".format(*c[:3]))
 def test_automatic_plain_persist_choice(oracle, case):
-    """The plain norm takes the persistent tile automatically only in 16-bit
-    storage, with 1024 lanes per row, rows without a ragged end and 256 rows
-    or more; the result is bit-equal to the forced row tile and matches the
-    oracle on sampled rows."""
+    """The plain norm takes the persistent tile automatically only with 1024
+    lanes per row and rows without a ragged end: in 16-bit storage over 256
+    rows or more, in f32 over 1024 rows or more at four loads per lane or
+    with a row that fills a two-load tile (n = 8192). The
+    result is bit-equal to the forced row tile and matches the oracle on
+    sampled rows."""
     st, n, rows, want = case
     label = f"auto-plain-{st}-n{n}-rows{rows}"
     say(label)
