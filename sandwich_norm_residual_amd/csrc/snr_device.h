@@ -351,10 +351,12 @@ pass_combine(const float *part, int chunks, int n, float eps, float *inv) {
 
 constexpr int kMaxDevices = 64;
 
-// Workgroups of `kernel` that the current device holds at once (cached per
-// device; 0 when the runtime cannot say).
-template <typename K>
-int64_t resident_blocks(K kernel, int block) {
+// Workgroups of kernel K (launched with `block` threads) that the current
+// device holds at once; 0 when the runtime cannot say. Cached per kernel and
+// device: K is a template argument, so every kernel has a cache of its own
+// (kernels of one signature must not share one).
+template <auto K>
+int64_t resident_blocks(int block) {
     static std::atomic<int64_t> cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -362,8 +364,8 @@ int64_t resident_blocks(K kernel, int block) {
     int64_t n = cache[dev].load(std::memory_order_relaxed);
     if (n > 0) return n;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block,
-                                                     0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, block, 0) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
                               dev) != hipSuccess)
         return 0;

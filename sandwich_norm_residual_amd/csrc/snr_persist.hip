@@ -190,7 +190,7 @@ template <int OP, int ST, int G, int VPT>
 hipError_t launch_persist(const RowArgs &p, int64_t row0, int64_t nrows,
                           hipStream_t stream) {
     int64_t blocks = nrows;
-    const int64_t resident = resident_blocks(persist_kernel<OP, ST, G, VPT>, G);
+    const int64_t resident = resident_blocks<&persist_kernel<OP, ST, G, VPT>>(G);
     if (resident > 0 && blocks > resident) blocks = resident;
     hipLaunchKernelGGL((persist_kernel<OP, ST, G, VPT>), dim3((unsigned int)blocks),
                        dim3(G), 0, stream, p, row0, row0 + nrows);

@@ -427,7 +427,7 @@ hipError_t launch_q8(const RowArgs &p, int64_t row0, int64_t nrows,
     constexpr int RPB = BLOCK / G;
     int64_t blocks = (nrows + RPB - 1) / RPB;
     if constexpr (q8_persistent(VPT * Codec<ST>::W)) {
-        const int64_t resident = resident_blocks(q8_kernel<ST, G, VPT>, BLOCK);
+        const int64_t resident = resident_blocks<&q8_kernel<ST, G, VPT>>(BLOCK);
         if (resident > 0 && blocks > resident) blocks = resident;
     }
     hipLaunchKernelGGL((q8_kernel<ST, G, VPT>), dim3((unsigned int)blocks),
