@@ -285,7 +285,20 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
     if (rem == 0 && (halves || wide_plain)) {
         const KernelEntry *pk =
             find_entry(op, st, w, KIND_PERSIST, best->g, best->vpt);
-        if (pk) c->k = pk;
+        // Not where the row tile holds every row at once and the persistent
+        // grid, whose larger register tile fits fewer workgroups, would take
+        // them in two or more rounds with little to overlap. At 6656 bf16
+        // (row tile 1024 resident; persistent 512 for the tail, 768 for its
+        // halves), persistent against row tile: the tail 8.63 -> 7.68 us at
+        // 640 rows and 11.27 -> 10.01 at 1024, norm_then_add 9.13 -> 7.84
+        // and add_then_norm 11.43 -> 10.34 at 1024 rows; f16 plain at 12288
+        // (512 against 256 resident) 5.65 -> 4.89 us at 300 rows. At 1024
+        // lanes (16384 bf16) it is mixed: the tail 10.30 -> 9.43 us at 300
+        // rows but 10.87 -> 11.33 at 512, add_then_norm 2-5% slower.
+        const int64_t rt = best->resident ? best->resident() : 0;
+        const int64_t pr = pk && pk->resident ? pk->resident() : 0;
+        const bool one_round = rt > 0 && pr > 0 && rows > pr && rows <= rt;
+        if (pk && !one_round) c->k = pk;
     }
     return SNR_OK;
 }

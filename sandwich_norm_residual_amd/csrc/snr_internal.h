@@ -88,6 +88,8 @@ using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
                                    int64_t row0, int64_t nrows, int chunks,
                                    int groups, hipStream_t);
 using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
+// Workgroups the current device holds at once (cached; 0 when unknown).
+using ResidentQuery = int64_t (*)();
 using MultiLaunch = hipError_t (*)(const MultiArgs &, int64_t row0,
                                    int64_t nrows, hipStream_t);
 using MultipassLaunch = hipError_t (*)(const RowArgs &, float *scratch,
@@ -111,6 +113,7 @@ struct KernelEntry {
     OccupancyQuery occupancy;
     MultipassLaunch multipass;
     MultiLaunch multi;   // several segments in one launch (row tile only)
+    ResidentQuery resident = nullptr;  // row tiles and persistent tiles
 };
 
 // The tables of compiled kernels: RMSNorm, the tail and its halves

@@ -580,6 +580,12 @@ hipError_t launch_rowtile(const RowArgs &p, int64_t row0, int64_t nrows,
 }
 
 template <int OP, int ST, int G, int VPT>
+int64_t resident_rowtile() {
+    return resident_blocks<&rowtile_kernel<OP, ST, G, VPT, false>>(
+        rowtile_block<G>());
+}
+
+template <int OP, int ST, int G, int VPT>
 hipError_t occupancy_rowtile(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
         blocks_per_cu, rowtile_kernel<OP, ST, G, VPT, false>,
@@ -676,7 +682,8 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 #define SNR_RT_M(OP, ST, G, VPT, M)                                         \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_ROWTILE, G, VPT,                 \
                 rowtile_block<G>(), &launch_rowtile<OP, ST, G, VPT>,        \
-                nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr, M}
+                nullptr, &occupancy_rowtile<OP, ST, G, VPT>, nullptr, M,    \
+                &resident_rowtile<OP, ST, G, VPT>}
 #define SNR_RT(OP, ST, G, VPT) SNR_RT_M(OP, ST, G, VPT, nullptr)
 #define SNR_RT_A(OP, ST, G, VPT)                                            \
     SNR_RT_M(OP, ST, G, VPT, (multi_for<OP, ST, G, VPT>()))

@@ -197,10 +197,15 @@ hipError_t launch_persist(const RowArgs &p, int64_t row0, int64_t nrows,
     return hipGetLastError();
 }
 
+template <int OP, int ST, int G, int VPT>
+int64_t resident_persist() {
+    return resident_blocks<&persist_kernel<OP, ST, G, VPT>>(G);
+}
+
 #define SNR_PERSIST(OP, ST, G, VPT)                                          \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_PERSIST, G, VPT, G,               \
                 &launch_persist<OP, ST, G, VPT>, nullptr, nullptr, nullptr,  \
-                nullptr}
+                nullptr, &resident_persist<OP, ST, G, VPT>}
 #define SNR_PERSIST_SHAPES(OP, ST)                                           \
     SNR_PERSIST(OP, ST, 128, 2), SNR_PERSIST(OP, ST, 256, 2),                \
     SNR_PERSIST(OP, ST, 512, 2), SNR_PERSIST(OP, ST, 1024, 1),               \

@@ -146,3 +146,41 @@ def test_automatic_plain_persist_choice(oracle, case):
     sub = {k: (val[pick] if isinstance(val, np.ndarray) and val.ndim == 2
                else val) for k, val in inp.items()}
     _check(oracle, "plain", sub, [got[0][pick]], label + "-sampled")
+
+
+@pytest.mark.parametrize("case", [("tail", "bf16", 6656, 1024, "rowtile:512:2:8"),
+                                  ("tail", "bf16", 6656, 1100, "persist:512:2:8"),
+                                  ("tail", "bf16", 6656, 512, "persist:512:2:8"),
+                                  ("norm_add", "f16", 6656, 1000, "rowtile:512:2:8"),
+                                  ("tail", "bf16", 16384, 300, "rowtile:1024:2:8"),
+                                  ("plain", "f16", 12288, 300, "rowtile:1024:2:8")],
+                         ids=lambda c: "{}-{}-n{}-rows{}".format(*c[:4]))
+def test_automatic_choice_one_round(oracle, case):
+    """Where the row tile holds every row at once on this GPU and the
+    persistent grid (a larger register tile, so fewer resident workgroups)
+    would not, the row tile is kept: on MI355X the 16-bit tail at 512 x 2
+    holds 1024 rows in one round of row tiles against 512 persistent
+    workgroups. Results bit-equal to the forced row tile; sampled rows
+    against the oracle. Also a regression test: resident counts were once
+    cached per kernel signature, so the first persistent kernel of a process
+    fixed the count for all of them."""
+    op, st, n, rows, want = case
+    label = f"auto-round-{op}-{st}-n{n}-rows{rows}"
+    say(label)
+    # a persistent kernel that holds fewer workgroups (256) runs first: the
+    # resident counts are kept per kernel, so it must not move the choice
+    warm = gen.random_plain(8, 1024 * 4 * 4, 36999)
+    with snr.forced_shape("persist", 1024, 4):
+        run_plain(warm)
+    inp = _inputs(op, st, rows, n, 36000 + rows + n)
+    got = _run(op, inp)
+    assert snr.last_shape() == want, (label, snr.last_shape())
+    _, g, v, _w = want.split(":")
+    with snr.forced_shape("rowtile", int(g), int(v)):
+        ref = _run(op, inp)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), label
+    pick = np.r_[0:3, rows // 2:rows // 2 + 3, rows - 3:rows]
+    sub = {k: (val[pick] if isinstance(val, np.ndarray) and val.ndim == 2
+               else val) for k, val in inp.items()}
+    _check(oracle, op, sub, [o[pick] for o in got], label + "-sampled")
