@@ -20,6 +20,12 @@
  *   its arguments has enqueued nothing. (SNR_ERR_HIP from a failed launch
  *   can follow earlier launches of the same call, e.g. of other row
  *   batches.)
+ * - HIP graphs: calls on rows that a register tile holds (up to 65536
+ *   elements) enqueue only kernels, so they can be recorded into a graph,
+ *   the first call of a process included (the host-side device and
+ *   occupancy queries it makes enqueue nothing). Wider rows use the
+ *   per-stream workspace, whose allocation on the first such call on a
+ *   stream cannot be captured: make that call once outside the capture.
  * - Reductions are deterministic: for a given (rows, n, dtype, dispatch
  *   shape) the result is bit-identical from run to run (fixed summation
  *   order, no floating-point atomics).

@@ -1,0 +1,80 @@
+"""A process whose very first library calls are made inside a HIP graph
+capture: the per-device facts and the kernels' resident workgroup counts are
+then queried during the capture (host queries only; nothing is enqueued by
+them). Run in a fresh Python process so that nothing is cached yet; the
+replays must equal eager calls made afterwards, bit for bit. The shapes
+cover a row tile, a persistent tile and the choice between them by resident
+counts (1024 rows of the 16-bit tail)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+SCRIPT = r"""
+import sys
+import torch
+sys.path.insert(0, ROOT)
+import sandwich_norm_residual_amd as snr
+
+dev = "cuda:0"
+g = torch.Generator(device="cpu").manual_seed(5)
+def rnd(*shape, dt=torch.float32):
+    return torch.randn(*shape, generator=g).to(dt).to(dev)
+
+cases = []
+# bf16 tail, 1024 rows of 6656: chosen by resident counts
+a, r = rnd(1024, 6656, dt=torch.bfloat16), rnd(1024, 6656, dt=torch.bfloat16)
+gp, gq = rnd(6656, dt=torch.bfloat16), rnd(6656, dt=torch.bfloat16)
+h, y = torch.empty_like(a), torch.empty_like(a)
+cases.append((lambda: snr.sandwich_tail(a, r, gp, 1e-8, gq, 1e-5, h_out=h, y_out=y), [h, y]))
+# f32 plain, 1024 rows of 16384: persistent 1024 x 4
+x, gx = rnd(1024, 16384), rnd(16384)
+yx = torch.empty_like(x)
+cases.append((lambda: snr.rmsnorm_fwd(x, gx, 1e-5, out=yx), [yx]))
+# f32 tail, 8 rows of 6656: row tile, gains loaded with the row
+a2, r2, g2, q2 = rnd(8, 6656), rnd(8, 6656), rnd(6656), rnd(6656)
+h2, y2 = torch.empty_like(a2), torch.empty_like(a2)
+cases.append((lambda: snr.sandwich_tail(a2, r2, g2, 1e-8, q2, 1e-5, h_out=h2, y_out=y2), [h2, y2]))
+
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):
+    for call, _ in cases:
+        call()
+shapes = []
+torch.cuda.synchronize()
+for rep in range(3):
+    for _, outs in cases:
+        for o in outs:
+            o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    got = [[o.clone() for o in outs] for _, outs in cases]
+    for (call, outs), gl in zip(cases, got):
+        call()
+        torch.cuda.synchronize()
+        shapes.append(snr.last_shape())
+        for o, gv in zip(outs, gl):
+            assert torch.equal(o.view(torch.int16) if o.dtype != torch.float32
+                               else o.view(torch.int32),
+                               gv.view(torch.int16) if gv.dtype != torch.float32
+                               else gv.view(torch.int32)), (rep, shapes[-1])
+print("first-call capture ok", sorted(set(shapes)), flush=True)
+"""
+
+
+def test_first_calls_inside_a_capture():
+    print("[gpu-case] first library calls inside a graph capture "
+          "(fresh process)", flush=True)
+    code = "ROOT = " + repr(ROOT) + "\n" + SCRIPT
+    proc = subprocess.run([sys.executable, "-c", code], cwd=ROOT,
+                          capture_output=True, text=True, timeout=110)
+    sys.stdout.write(proc.stdout[-2000:])
+    sys.stderr.write(proc.stderr[-2000:])
+    assert proc.returncode == 0, proc.returncode
+    assert "first-call capture ok" in proc.stdout
