@@ -35,7 +35,7 @@ CASES = [(op, dtype, g, vpt)
          for op in ("plain", "tail", "add_norm")
          for dtype in ("f32", "bf16", "f16")
          for g, vpt in TILES]
-MULTI_CASES = [(dtype, g, vpt) for dtype in ("f32", "bf16")
+MULTI_CASES = [(dtype, g, vpt) for dtype in ("f32", "bf16", "f16")
                for g, vpt in TILES]
 
 
