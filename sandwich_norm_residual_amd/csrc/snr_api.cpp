@@ -257,6 +257,17 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
         c->chunks = split_chunks(c->k, nv);
         return SNR_OK;
     }
+    // Launches of a few rows are a chain of dependent memory round trips.
+    // There the 512 x 4 tile measured faster than 1024 x 2 in f32 for the
+    // tail, the plain norm and norm_then_add (1 to 16 rows of 4608, 6656
+    // and 8192: tail 3.25 -> 3.12 us at one row of 6656, plain 2.28 ->
+    // 2.21, norm_then_add 2.49 -> 2.41), and slower for add_then_norm (2.78
+    // -> 2.93), whose first phase also stores the sum.
+    if (st == ST_F32 && op != OP_ADD_NORM && best->g == 1024 &&
+        best->vpt == 2 && rows > 0 && rows <= kEarlyBlocks) {
+        const KernelEntry *half = find_entry(op, st, w, KIND_ROWTILE, 512, 4);
+        if (half && 512LL * 4 >= nv) best = half;
+    }
     c->k = best;
     // The persistent form of the same tile (loads of the next row in flight
     // through this row's reductions) measured faster for:

@@ -19,8 +19,9 @@ torch = pytest.importorskip("torch")
 
 import sandwich_norm_residual_amd as snr  # noqa: E402
 from sandwich_norm_residual_amd import inputs as gen  # noqa: E402
-from gpu_helpers import (check_add_norm, check_plain, check_tail, dev,  # noqa: E402
-                         host_f64, say)
+from gpu_helpers import (check_add_norm, check_norm_add, check_plain,  # noqa: E402
+                         check_tail, dev, host_f64, run_add_norm,
+                         run_norm_add, run_plain, run_tail, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +168,52 @@ def test_multi_early_and_late_gains_agree(oracle, case):
         inp = {"x": xs[s][:few], "gamma": gs[s], "eps": epss[s],
                "dtype": dtype}
         check_plain(oracle, inp, host_f64(part[s]), f"{label}-seg{s}")
+
+
+@pytest.mark.parametrize("case", [("tail", 1, 6656, "rowtile:512:4:4"),
+                                  ("tail", 16, 8192, "rowtile:512:4:4"),
+                                  ("tail", 17, 6656, "rowtile:1024:2:4"),
+                                  ("plain", 8, 4608, "rowtile:512:4:4"),
+                                  ("norm_add", 2, 6656, "rowtile:512:4:4"),
+                                  ("add_norm", 1, 6656, "rowtile:1024:2:4")],
+                         ids=lambda c: "{}-rows{}-n{}".format(*c[:3]))
+def test_decode_tile_choice(oracle, case):
+    """f32 launches of at most 16 rows that would take the 1024 x 2 tile
+    take 512 x 4 instead, except add_then_norm; the result matches the
+    oracle. (The two tiles sum each row's squares in different orders, so
+    their last bits may differ.)"""
+    op, rows, n, want = case
+    label = f"decode-tile {op} rows={rows} n={n}"
+    say(label)
+    rng = gen.rng_for(62000 + rows + n)
+    if op == "plain":
+        inp = {"x": _rows(rng, rows, n, "f32"), "gamma": _gain(rng, n, "f32"),
+               "eps": 1e-5, "dtype": "f32"}
+        run = lambda: [run_plain(inp)[0]]
+    elif op == "tail":
+        inp = {"a": _rows(rng, rows, n, "f32"),
+               "r": _rows(rng, rows, n, "f32", 3.0),
+               "gamma_post": _gain(rng, n, "f32"),
+               "gamma_pre": _gain(rng, n, "f32"), "eps_post": 1e-8,
+               "eps_pre": 1e-5, "dtype": "f32"}
+        run = lambda: list(run_tail(inp))
+    elif op == "norm_add":
+        inp = {"a": _rows(rng, rows, n, "f32"),
+               "b": _rows(rng, rows, n, "f32", 2.0),
+               "gamma": _gain(rng, n, "f32"), "eps": 1e-8, "dtype": "f32"}
+        run = lambda: [run_norm_add(inp)]
+    else:
+        inp = {"a": _rows(rng, rows, n, "f32"),
+               "b": _rows(rng, rows, n, "f32", 0.5),
+               "gamma": _gain(rng, n, "f32"), "eps": 1e-5, "dtype": "f32"}
+        run = lambda: list(run_add_norm(inp))
+    got = run()
+    assert snr.last_shape() == want, (label, snr.last_shape())
+    if op == "plain":
+        check_plain(oracle, inp, got[0], label)
+    elif op == "tail":
+        check_tail(oracle, inp, got[0], got[1], label)
+    elif op == "norm_add":
+        check_norm_add(oracle, inp, got[0], None, label)
+    else:
+        check_add_norm(oracle, inp, got[0], got[1], label)
