@@ -262,7 +262,9 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
     // tail, the plain norm and norm_then_add (1 to 16 rows of 4608, 6656
     // and 8192: tail 3.25 -> 3.12 us at one row of 6656, plain 2.28 ->
     // 2.21, norm_then_add 2.49 -> 2.41), and slower for add_then_norm (2.78
-    // -> 2.93), whose first phase also stores the sum.
+    // -> 2.93), whose first phase also stores the sum. What helps is leaving
+    // the 16-wavefront workgroup: halving 512 x 2 into 256 x 4 was 5-15%
+    // slower for every operation (one row of 4096: tail 2.68 -> 2.85 us).
     if (st == ST_F32 && op != OP_ADD_NORM && best->g == 1024 &&
         best->vpt == 2 && rows > 0 && rows <= kEarlyBlocks) {
         const KernelEntry *half = find_entry(op, st, w, KIND_ROWTILE, 512, 4);
