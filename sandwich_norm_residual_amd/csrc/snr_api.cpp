@@ -311,7 +311,12 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
         const int64_t rt = best->resident ? best->resident() : 0;
         const int64_t pr = pk && pk->resident ? pk->resident() : 0;
         const bool one_round = rt > 0 && pr > 0 && rows > pr && rows <= rt;
-        if (pk && !one_round) c->k = pk;
+        // Nor for a few rows at 1024 lanes, where the row tile with its gains
+        // loaded with the row is as fast or faster (one row of 12288 bf16:
+        // tail 4.25 -> 3.70 us; of 16384 within 2%), while at 512 lanes the
+        // persistent tile is (one row of 6656 bf16: 2.92 against 3.32 us).
+        const bool few_wide = best->g == 1024 && rows > 0 && rows <= kEarlyBlocks;
+        if (pk && !one_round && !few_wide) c->k = pk;
     }
     return SNR_OK;
 }
