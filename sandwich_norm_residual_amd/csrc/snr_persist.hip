@@ -167,6 +167,12 @@ persist_kernel(RowArgs p, int64_t row0, int64_t row_end) {
     // for why both matter to the compiler's waits).
     const int64_t trips = (row_end - first + stride - 1) / stride;
     u32x4 a0[VPT], b0[VPT], a1[VPT], b1[VPT];
+    if (first + stride >= row_end) {
+        // one row for this workgroup: nothing to prefetch
+        load_rows(a0, b0, first);
+        process(a0, b0, first, 0);
+        return;
+    }
     load_rows(a0, b0, first);
     load_rows(a1, b1, first + stride);
     process(a0, b0, first, 0);
