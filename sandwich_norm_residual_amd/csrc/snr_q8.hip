@@ -323,6 +323,12 @@ q8_kernel(RowArgs p, int64_t row0, int64_t row_end) {
                 rg, i < nv ? 16u * i : kOutOfRange, 0, 0);
         }
         u32x4 buf[NB][VPT];
+        if (trips == 1) {
+            // one row block for this workgroup: nothing to prefetch
+            load_rows(buf[0], first);
+            quant_rows(buf[0], gv, first, red[0]);
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < PD; ++r) load_rows(buf[r], first + r * stride);
         // (the peeled steps run even for a dead block, which reads zeros and
