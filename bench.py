@@ -349,6 +349,39 @@ def capture_steps(step, count: int, torch):
     return graph
 
 
+def host_cpus() -> dict:
+    """The host's CPUs as this process sees them: the online count, the
+    affinity mask, the CPU model, and the oracle's thread count (one thread
+    per CPU in the affinity mask, unless OMP_NUM_THREADS states a smaller
+    CPU share for this process)."""
+    aff = sorted(os.sched_getaffinity(0))
+    ranges, start = [], None
+    for i, c in enumerate(aff):
+        if start is None:
+            start = c
+        if i + 1 == len(aff) or aff[i + 1] != c + 1:
+            ranges.append(f"{start}-{c}" if c > start else f"{c}")
+            start = None
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cap = None
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "")) or None
+    except ValueError:
+        cap = None
+    threads = len(aff) if not cap else max(1, min(len(aff), cap))
+    return {"nproc": os.cpu_count(), "affinity": len(aff),
+            "mask": ",".join(ranges), "model": model, "cap": cap,
+            "threads": threads}
+
+
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
     """The f64 oracle as it stands, rows split across host threads (ctypes
     releases the GIL), repeated over the full workload for about `seconds`."""
@@ -358,7 +391,8 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
 
     import oracle
     O = oracle.load()
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    hw = host_cpus()
+    cores = hw["threads"]
     rows = cfg.rows
     bounds = [(rows * i // cores, rows * (i + 1) // cores)
               for i in range(cores)]
@@ -420,24 +454,23 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
                 break
     dt = time.perf_counter() - t0
     gbs = algorithmic_bytes(cfg) * passes / dt / 1e9
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    model = hw["model"]
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": len(bounds),
             "kind": "oracle",
             "single_core_value": round(gbs1, 3),
+            "nproc": hw["nproc"], "affinity_cpus": hw["affinity"],
+            "affinity_mask": hw["mask"], "cpu_model": model,
+            "thread_cap": hw["cap"],
             "sample": (f"{passes} full passes over {cfg.name} "
                        f"({rows} rows) in {dt:.1f} s, scalar f64 C oracle, "
                        f"rows split over {len(bounds)} threads; "
                        f"rows/s {rows * passes / dt:.4g}; one core: "
                        f"{rows1} rows in {dt1:.1f} s, {gbs1:.3g} GB/s, "
-                       f"rows/s {rows1 / dt1:.4g}; cpu: {model}")}
+                       f"rows/s {rows1 / dt1:.4g}; cpu: {model}; nproc "
+                       f"{hw['nproc']}, {hw['affinity']} CPUs in the "
+                       f"affinity mask ({hw['mask']})"
+                       + (f", OMP_NUM_THREADS={hw['cap']}" if hw["cap"]
+                          else ""))}
 
 
 def main() -> int:
@@ -452,6 +485,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=None,
                     help="rotating buffer sets (default: at least 3 and 1 GiB "
                          "of step traffic together, at most 64)")
+    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+                    help="untimed steps back to back for this long before "
+                         "the timed region (reported as prewarm_ms)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle CPU baseline")
@@ -517,23 +553,46 @@ def main() -> int:
         calls = max(1, args.steps // unit)
         steps = calls * unit
 
-        # whole-job throughput: K back-to-back steps, synchronised both sides
+        # Pre-warm: steps back to back for a fixed stretch of wall time
+        # before the timed region (untimed, beyond the W warm-up steps), so
+        # that a short timed region meets the GPU's clocks at steady state
+        # rather than ramping up from idle.
+        # The host waits on the batch before last, so the GPU always has a
+        # batch queued and never idles.
+        prewarm_calls = 0
+        prev = None
+        tp = time.perf_counter()
+        while time.perf_counter() - tp < args.prewarm_ms * 1e-3:
+            for _ in range(16):
+                run(prewarm_calls)
+                prewarm_calls += 1
+            ev_batch = torch.cuda.Event()
+            ev_batch.record(stream)
+            if prev is not None:
+                prev.synchronize()
+            prev = ev_batch
+        torch.cuda.synchronize()
+        prewarm_s = time.perf_counter() - tp
+
+        # whole-job throughput: K back-to-back steps, synchronised both
+        # sides. Inside the same region, one event pair on the launch stream
+        # brackets calls 1 .. K-1 (the first call's host launch latency, when
+        # the GPU has nothing queued, stays outside the pair): their average
+        # is the per-launch duration.
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         for i in range(calls):
             run(i)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-
-        # average launch duration: one event pair on the launch stream around
-        # K back-to-back launches
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(calls):
-            run(i)
+            if i == 0:
+                e0.record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        mean_us = e0.elapsed_time(e1) * 1e3 / steps
+        wall = time.perf_counter() - t0
+        if calls > 1:
+            mean_us = e0.elapsed_time(e1) * 1e3 / ((calls - 1) * unit)
+        else:
+            mean_us = wall * 1e6 / steps
 
         # spread of single launches (each bracketed by its own events, which
         # adds the events' own overhead to every sample; with graphs, the
@@ -619,6 +678,8 @@ def main() -> int:
                    "algorithmic_bytes_per_step": nbytes},
         "rows_per_s": round(cfg.rows * steps / wall, 1),
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "prewarm_ms": round(prewarm_s * 1e3, 1),
+        "prewarm_steps": prewarm_calls * unit,
         "kernel_us": {"mean_over_timed_region": round(mean_us, 3),
                       "single_launch_median": round(med_us, 3),
                       "single_launch_p10": round(q[0], 3),

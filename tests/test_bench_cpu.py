@@ -166,3 +166,19 @@ def test_stream_probe_library_exports():
     assert lib.stream_probe(0, None, 16, 16, 16, 0, None) == -1
     assert lib.stream_probe(3, 16, 8, 16, 16, 0, None) == -1
     assert lib.stream_probe(0, 16, None, None, 16, 0, None) == -1
+
+
+def test_host_cpus_reports_the_affinity_mask(monkeypatch):
+    """The CPU baseline's thread count is the affinity mask's CPU count,
+    capped by OMP_NUM_THREADS when that states a smaller share, and the
+    mask is reported as ranges."""
+    monkeypatch.setattr(bench.os, "sched_getaffinity",
+                        lambda pid: {0, 1, 2, 3, 8, 10, 11})
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    hw = bench.host_cpus()
+    assert hw["affinity"] == 7 and hw["threads"] == 7
+    assert hw["mask"] == "0-3,8,10-11"
+    monkeypatch.setenv("OMP_NUM_THREADS", "4")
+    assert bench.host_cpus()["threads"] == 4
+    monkeypatch.setenv("OMP_NUM_THREADS", "64")
+    assert bench.host_cpus()["threads"] == 7
