@@ -223,7 +223,7 @@ def kernel_sources(cfg) -> list:
     """The source files the workload's kernels are built from."""
     csrc = os.path.join(ROOT, "sandwich_norm_residual_amd", "csrc")
     main = (("snr_q8.hip",) if cfg.kind == "q8"
-            else ("snr_kernels.hip", "snr_persist.hip"))
+            else ("snr_kernels.hip", "snr_persist.hip", "snr_split.hip"))
     return [os.path.join(csrc, f)
             for f in ("snr_internal.h", "snr_device.h") + main]
 

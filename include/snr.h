@@ -8,11 +8,16 @@
  *   memory (row i starts at element i*n); gains are dense [n] vectors shared
  *   by all rows. There is no stride argument.
  * - All pointers are device pointers owned by the caller. The library never
- *   frees or retains them. It owns only a per-(device, stream) workspace of
- *   about 10 MB, for the partial sums of the split-row and multi-pass
- *   kernels (rows wider than 65536 elements): allocated by the first such
- *   call on that stream, left zeroed by every launch, kept until the process
- *   exits. Every other shape allocates nothing.
+ *   frees or retains them. It owns only workspaces of 1 MiB of device
+ *   memory each, for the partial sums of the split-row and multi-pass
+ *   kernels (rows wider than 65536 elements): at most 8 per device, each
+ *   bound to one stream at a time, allocated by the first such call on a
+ *   stream that finds none free, kept until the process exits (so at most
+ *   8 MiB per device however many streams are used). When a ninth stream
+ *   needs one, it takes the least recently used workspace, and its launches
+ *   wait on the GPU for that workspace's last use on the other stream to
+ *   finish (the library records an event after each use), so uses of one
+ *   workspace never overlap. Every other shape allocates nothing.
  * - Calls are asynchronous: they validate the arguments, enqueue kernels on
  *   `stream` (NULL = the legacy default stream of the current device; any
  *   other stream must belong to the current device) and return. Execution faults surface at the caller's next synchronisation.
@@ -23,9 +28,13 @@
  * - HIP graphs: calls on rows that a register tile holds (up to 65536
  *   elements) enqueue only kernels, so they can be recorded into a graph,
  *   the first call of a process included (the host-side device and
- *   occupancy queries it makes enqueue nothing). Wider rows use the
- *   per-stream workspace, whose allocation on the first such call on a
- *   stream cannot be captured: make that call once outside the capture.
+ *   occupancy queries it makes enqueue nothing). Wider rows use a
+ *   workspace: under capture a call may use only the workspace its stream
+ *   already holds (make one call on that stream outside the capture first;
+ *   otherwise the call returns SNR_ERR_CAPTURE and enqueues nothing), and
+ *   that workspace then stays with the stream for the life of the process.
+ *   Replays of such a graph must not overlap one another or wide-row calls
+ *   on the capture stream (replay them on that stream, or order them).
  * - Reductions are deterministic: for a given (rows, n, dtype, dispatch
  *   shape) the result is bit-identical from run to run (fixed summation
  *   order, no floating-point atomics).
@@ -71,13 +80,17 @@ enum {
     SNR_ERR_EPS = 4,       /* an epsilon is not finite or not > 0 */
     SNR_ERR_ALIAS = 5,     /* buffers overlap other than in an allowed way */
     SNR_ERR_ALIGN = 6,     /* a pointer is not aligned to its element size */
-    SNR_ERR_WORKSPACE = 7, /* the per-stream workspace could not be
-                              allocated, or a forced split shape cannot
-                              keep every chunk of a row co-resident */
+    SNR_ERR_WORKSPACE = 7, /* a workspace could not be allocated, every
+                              workspace of the device is held by a captured
+                              graph, or a forced split shape cannot keep
+                              every chunk of a row co-resident */
     SNR_ERR_HIP = 8,       /* a HIP runtime call failed; see
                               snr_last_hip_error() */
-    SNR_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU, or
+    SNR_ERR_DEVICE = 9,    /* the current device is not a gfx950 GPU, or
                               `stream` belongs to another device */
+    SNR_ERR_CAPTURE = 10   /* rows wider than 65536 elements under HIP
+                              graph capture on a stream that holds no
+                              workspace yet (see "HIP graphs" above) */
 };
 
 /*
@@ -278,10 +291,12 @@ SNR_API int snr_last_hip_error(void);
  *                             workgroups loads the gains together with the
  *                             row (one memory round trip fewer; the same
  *                             results bit for bit)
- *          SNR_SHAPE_SPLIT    the row is cut into chunks of 256 x `vpt`
- *                             vectors, one workgroup per chunk, joined by a
- *                             two-phase cross-workgroup reduction; every
- *                             chunk of a row must be co-resident
+ *          SNR_SHAPE_SPLIT    the row is cut into chunks of 4096 elements
+ *                             (256 lanes x 4 vectors f32, x 2 vectors
+ *                             16-bit), one workgroup per chunk, joined by a
+ *                             cross-workgroup reduction through device
+ *                             memory; every chunk of a row must be
+ *                             co-resident (g and vpt are ignored)
  *          SNR_SHAPE_MULTIPASS rows wider than that: per-chunk partial sums,
  *                             a per-row combine and an apply pass through
  *                             device memory (reads the row twice; the tail
@@ -300,7 +315,7 @@ SNR_API int snr_last_hip_error(void);
  * row (g * vpt loads < row length) or that has no compiled kernel returns
  * SNR_ERR_SHAPE from the call. snr_last_shape writes "rowtile:g:vpt:width",
  * "persist:g:vpt:width", "split:256:vpt:width:chunks" or
- * "multipass:256:8:width:chunks" (width =
+ * "multipass:256:16:width:chunks" (width =
  * elements per 128-bit vector) of
  * the calling thread's most recent successful launch into buf
  * (NUL-terminated).
@@ -316,17 +331,33 @@ SNR_API int snr_force_shape(int kind, int g, int vpt);
 SNR_API int snr_last_shape(char *buf, int len);
 
 /*
- * Split-row wait watchdog. The split-row kernels wait for the partial sums
- * of the other workgroups of their row with a bounded spin; if the bound is
- * ever exceeded the kernel stops waiting, records the event in the stream's
- * workspace and finishes (its outputs are then invalid). This returns the
- * number of such events recorded on (current device, stream) and clears the
- * count. It synchronises the stream. 0 means every wait completed normally.
- * When the count is not 0 the stream's workspace is cleared again before
- * this returns, so later calls start from a clean state.
- * The environment variable SNR_SPLIT_SPIN_LIMIT (a positive integer, read at
+ * Split-row kernels and their wait watchdog. Rows wider than any register
+ * tile (65536 elements) are cut into chunks of 4096 elements, one
+ * workgroup per chunk, whose partial sums meet through the workspace. The
+ * grid is at most the number of workgroups the device holds at once, and
+ * the library never lets two split-row launches overlap on a device (it
+ * orders each one after the previous one, on any stream, with an event);
+ * the kernels assume every workgroup of their grid becomes resident. By
+ * default they are ordinary launches; with the environment variable
+ * SNR_SPLIT_COOPERATIVE set (not "0") they are cooperative launches, which
+ * the runtime admits only when the whole grid fits and then keeps resident,
+ * at a cost of about 14 us per launch. A workgroup waits for the partial
+ * sums of the other chunks of its row with a bounded spin; if the bound is
+ * ever exceeded (only if some workgroups of the grid could not become
+ * resident for seconds), the kernel stops waiting, counts the event in the
+ * workspace, writes NaN to every output of that row, and finishes. Later
+ * calls are not affected: each launch tags its partial sums with a number
+ * no earlier launch left in the workspace, so nothing an earlier launch
+ * left behind is ever taken for a later launch's. This returns the number
+ * of such events counted in the workspace (current device, stream) holds,
+ * and clears the count. It synchronises the stream and the workspace's last
+ * use. 0 means every wait completed normally (or the stream holds no
+ * workspace).
+ * The environment variable SNR_SPLIT_SPIN_LIMIT (an integer >= 0, read at
  * each split-row launch) replaces the default bound of 2^22 polls; tests use
- * a tiny value to force the bounded-wait path.
+ * 0 to make every wait give up at once. SNR_SPLIT_EPOCH (read when a
+ * workspace is created) sets its starting tag number; tests use a value
+ * near 2^31 - 1 to exercise the wrap of the tag numbers.
  */
 SNR_API int snr_split_timeouts(hipStream_t stream, int64_t *count);
 

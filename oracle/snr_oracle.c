@@ -114,10 +114,10 @@ int snr_oracle_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma,
  * The dual-epsilon sandwich tail, one row at a time. It follows the sandwich
  * order of "RMSNorm and the dual-epsilon sandwich", section 12.2 (post-norm on
  * the sub-block output before the residual add, then the next pre-norm on the
- * updated stream), and the fused tail of section 12.4.3:
- *   hidden += rms_norm(src, eps1) * weight1
- *   output  = rms_norm(hidden, eps2) * weight2
- * With a = src (sub-block output), r = the residual stream before the add:
+ * updated stream), and the fused tail of section 12.4.3, which adds the
+ * post-normed sub-block output into the residual stream in place and then
+ * pre-norms the updated stream with the second epsilon and gain. With a =
+ * the sub-block output and r = the residual stream before the add:
  *   d_a = sqrt(mean(a^2) + eps_post)
  *   p_j = a_j / d_a * gamma_post_j           (post-norm output)
  *   h_j = r_j + p_j                          (residual add; updated stream)

@@ -26,6 +26,7 @@ SNR_ERR_ALIGN = 6
 SNR_ERR_WORKSPACE = 7
 SNR_ERR_HIP = 8
 SNR_ERR_DEVICE = 9
+SNR_ERR_CAPTURE = 10
 
 SHAPE_AUTO = 0
 SHAPE_ROWTILE = 1

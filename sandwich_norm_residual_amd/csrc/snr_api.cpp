@@ -15,6 +15,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "snr.h"
 #include "snr_internal.h"
@@ -80,57 +81,179 @@ int current_device(hipStream_t stream, int *dev, DeviceInfo *info) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-row workspace, one per (device, stream)
+// Workspaces: the split-row kernels' tagged partial-sum slots and the
+// multi-pass kernels' scratch, 1 MiB of device memory each:
+//   [0, 256)                 header: the count of waits that gave up
+//   [256, 256 + 256 KiB)     32768 slots of 8 bytes (split-row kernels)
+//   [256 + 256 KiB, 1 MiB)   196544 floats (multi-pass partial sums and
+//                            inverse norms)
+// A device has at most kMaxWorkspaces of them, each bound to one stream at a
+// time. Every use of a workspace on an eagerly running stream is enqueued
+// after a wait on the event recorded after its previous use (on whichever
+// stream that was) and followed by a new record, all under g_ws_mu, so two
+// uses of one workspace never overlap on the GPU. A new stream takes a free
+// workspace, or the least recently used one that no captured graph holds.
+// A stream that is being captured into a HIP graph may use only the
+// workspace it already holds (allocation and cross-stream waits cannot be
+// captured); that workspace is then pinned to it for the life of the
+// process, because the graph may be replayed at any time.
 // ---------------------------------------------------------------------------
-constexpr int64_t kSlotCap = int64_t(1) << 18;  // partial slots per set
-constexpr int64_t kRowCap = int64_t(1) << 18;   // rows per launch
-constexpr uint32_t kSpinLimit = 1u << 22;       // polls before giving up
-constexpr int64_t kMultiFloats = int64_t(1) << 20;  // multi-pass scratch
+constexpr int64_t kWorkspaceBytes = int64_t(1) << 20;
+constexpr int64_t kHeaderBytes = 256;
+constexpr int64_t kSlotWords = 32768;
+constexpr int64_t kMultiOffset = kHeaderBytes + kSlotWords * 8;
+constexpr int64_t kMultiFloats = (kWorkspaceBytes - kMultiOffset) / 4;
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up
+constexpr int kMaxWorkspaces = 8;           // per device
 
 struct Workspace {
     void *base = nullptr;
-    int64_t words = 0;
-    SplitState st{};
-    float *multi = nullptr;  // multi-pass partial sums and inverse norms
+    hipEvent_t last_use = nullptr;  // recorded after each eager use
+    hipStream_t stream = nullptr;   // the stream it is bound to
+    uint64_t stamp = 0;             // last use, for eviction
+    bool pinned = false;            // captured into a graph
+    uint32_t next_tag = 1;          // the next split-row launch's tag
 };
 
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::mutex g_ws_mu;   // guards g_ws, g_ws_clock and every workspace use
+std::map<int, std::vector<Workspace>> g_ws;
+uint64_t g_ws_clock = 0;
 
-int get_workspace(int dev, hipStream_t stream, Workspace *out) {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    auto key = std::make_pair(dev, stream);
-    auto it = g_ws.find(key);
-    if (it == g_ws.end()) {
-        Workspace w;
-        const int64_t slot_bytes = 2 * kSlotCap * 8;
-        const int64_t depart_bytes = 2 * kRowCap * 4;
-        const int64_t multi_bytes = kMultiFloats * 4;
-        const int64_t bytes = slot_bytes + depart_bytes + 256 + multi_bytes;
-        hipError_t e = hipMalloc(&w.base, (size_t)bytes);
-        if (e != hipSuccess) {
-            t_last_hip_error = (int)e;
-            return SNR_ERR_WORKSPACE;
-        }
-        w.words = bytes / 4;
-        e = zero_words(w.base, w.words, stream);
-        if (e != hipSuccess) {
-            (void)hipFree(w.base);
-            return hip_fail(e);
-        }
-        char *b = static_cast<char *>(w.base);
-        w.st.slots = reinterpret_cast<unsigned long long *>(b);
-        w.st.depart = reinterpret_cast<unsigned int *>(b + slot_bytes);
-        w.st.timeouts =
-            reinterpret_cast<unsigned int *>(b + slot_bytes + depart_bytes);
-        w.st.slot_cap = kSlotCap;
-        w.st.row_cap = kRowCap;
-        w.st.spin_limit = kSpinLimit;
-        w.multi = reinterpret_cast<float *>(b + slot_bytes + depart_bytes +
-                                            256);
-        it = g_ws.emplace(key, w).first;
+SplitState split_state(void *base) {
+    char *b = static_cast<char *>(base);
+    SplitState st{};
+    st.hdr = reinterpret_cast<unsigned int *>(b);
+    st.slots = reinterpret_cast<unsigned long long *>(b + kHeaderBytes);
+    st.slot_cap = kSlotWords;
+    st.spin_limit = kSpinLimit;
+    // Test hook: a small poll budget (0: none) forces the bounded-wait path.
+    if (const char *lim = std::getenv("SNR_SPLIT_SPIN_LIMIT")) {
+        char *end = nullptr;
+        const long v = std::strtol(lim, &end, 10);
+        if (end != lim && v >= 0 && v <= (long)UINT32_MAX)
+            st.spin_limit = (uint32_t)v;
     }
-    *out = it->second;
+    return st;
+}
+
+float *multi_scratch(void *base) {
+    return reinterpret_cast<float *>(static_cast<char *>(base) + kMultiOffset);
+}
+
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess &&
+           cs != hipStreamCaptureStatusNone;
+}
+
+// A zeroed workspace. Its first tag is 1, or SNR_SPLIT_EPOCH + 1 when that
+// is given (a test hook: a value near 2^31 - 1 makes the next launches wrap
+// the tags).
+int new_workspace(hipStream_t stream, Workspace *w) {
+    hipError_t e = hipMalloc(&w->base, (size_t)kWorkspaceBytes);
+    if (e != hipSuccess) {
+        t_last_hip_error = (int)e;
+        w->base = nullptr;
+        return SNR_ERR_WORKSPACE;
+    }
+    e = hipEventCreateWithFlags(&w->last_use, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = fill_words(w->base, kWorkspaceBytes / 4, 0u, stream);
+    if (e != hipSuccess) {
+        if (w->last_use) (void)hipEventDestroy(w->last_use);
+        (void)hipFree(w->base);
+        *w = Workspace{};
+        return hip_fail(e);
+    }
+    if (const char *ep = std::getenv("SNR_SPLIT_EPOCH"))
+        w->next_tag = (uint32_t)std::strtoul(ep, nullptr, 10) + 1u;
+    return SNR_OK;
+}
+
+// The tag of the next split-row launch on a workspace whose slots are at
+// `slots` (caller holds g_ws_mu). Eager launches take 1, 2, ...,
+// 2^31 - 1; before these wrap to 1 again, every slot is cleared on the
+// stream (after every earlier use of the workspace, which the caller's
+// stream is ordered after). Launches recorded into a graph all take
+// kCapturedTag, outside that range, and the caller records a clear of the
+// launch's slots before each of them: a replay's leftovers never carry an
+// eager launch's tag, and every replay starts from cleared slots.
+constexpr uint32_t kCapturedTag = 0x80000000u;
+
+hipError_t take_tag(Workspace *w, unsigned long long *slots, bool eager,
+                    hipStream_t stream, uint32_t *tag) {
+    if (!eager) {
+        *tag = kCapturedTag;
+        return hipSuccess;
+    }
+    if (w->next_tag == 0 || w->next_tag >= kCapturedTag) {
+        const hipError_t e = fill_words(slots, kSlotWords * 2, 0u, stream);
+        if (e != hipSuccess) return e;
+        w->next_tag = 1;
+    }
+    *tag = w->next_tag++;
+    return hipSuccess;
+}
+
+// The workspace `stream` uses on device `dev` (caller holds g_ws_mu). Sets
+// *eager to whether the stream runs eagerly (not under capture); for an
+// eager stream the caller waits on w->last_use before its launches and
+// records it after them.
+int acquire_workspace(int dev, hipStream_t stream, Workspace **out,
+                      bool *eager) {
+    const bool cap = capturing(stream);
+    *eager = !cap;
+    std::vector<Workspace> &pool = g_ws[dev];
+    for (Workspace &w : pool)
+        if (w.stream == stream) {
+            if (cap) w.pinned = true;
+            w.stamp = ++g_ws_clock;
+            *out = &w;
+            return SNR_OK;
+        }
+    if (cap) return SNR_ERR_CAPTURE;
+    Workspace *w = nullptr;
+    if ((int)pool.size() < kMaxWorkspaces) {
+        pool.reserve(kMaxWorkspaces);   // pointers into the pool stay valid
+        Workspace fresh;
+        const int rc = new_workspace(stream, &fresh);
+        if (rc != SNR_OK) return rc;
+        pool.push_back(fresh);
+        w = &pool.back();
+    } else {
+        for (Workspace &c : pool)
+            if (!c.pinned && (!w || c.stamp < w->stamp)) w = &c;
+        if (!w) return SNR_ERR_WORKSPACE;   // every workspace is pinned
+    }
+    w->stream = stream;
+    w->stamp = ++g_ws_clock;
+    *out = w;
+    return SNR_OK;
+}
+
+// Cooperative launches of the split-row kernels (SNR_SPLIT_COOPERATIVE set
+// and not "0"): the runtime then checks and guarantees that the whole grid
+// is resident, at a cost of about 14 us per launch on MI355X. By default the
+// launch is ordinary, with the grid sized to the occupancy-derived resident
+// count and split-row launches serialised per device.
+bool split_cooperative() {
+    const char *v = std::getenv("SNR_SPLIT_COOPERATIVE");
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+// The event recorded after the latest eager split-row launch on a device
+// (caller holds g_ws_mu).
+std::map<int, hipEvent_t> g_split_serial;
+
+int split_serial_event(int dev, hipEvent_t **out) {
+    auto it = g_split_serial.find(dev);
+    if (it == g_split_serial.end()) {
+        hipEvent_t ev = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e);
+        it = g_split_serial.emplace(dev, ev).first;
+    }
+    *out = &it->second;
     return SNR_OK;
 }
 
@@ -166,6 +289,7 @@ struct Choice {
 const KernelEntry *table_for(int op, int kind, int *count) {
     if (op == OP_NORM_Q8) return q8_kernel_table(count);
     if (kind == KIND_PERSIST) return persist_kernel_table(count);
+    if (kind == KIND_SPLIT) return split_kernel_table(count);
     return kernel_table(count);
 }
 
@@ -173,10 +297,13 @@ const KernelEntry *find_entry(int op, int st, int w, int kind, int g,
                               int vpt) {
     int count = 0;
     const KernelEntry *t = table_for(op, kind, &count);
+    // the split-row kernels have one geometry per storage type
     const bool by_g = kind == KIND_ROWTILE || kind == KIND_PERSIST;
+    const bool by_vpt = kind != KIND_SPLIT;
     for (int i = 0; i < count; ++i)
         if (t[i].op == op && t[i].storage == st && t[i].width == w &&
-            t[i].kind == kind && (!by_g || t[i].g == g) && t[i].vpt == vpt)
+            t[i].kind == kind && (!by_g || t[i].g == g) &&
+            (!by_vpt || t[i].vpt == vpt))
             return &t[i];
     return nullptr;
 }
@@ -251,7 +378,7 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
     if (!best) {
         // no register tile holds the row: split it across workgroups (or,
         // for an operation without a split kernel, use the multi-pass one)
-        c->k = find_entry(op, st, w, KIND_SPLIT, 0, 8);
+        c->k = find_entry(op, st, w, KIND_SPLIT, 0, 0);
         if (!c->k) c->k = find_entry(op, st, w, KIND_MULTIPASS, 0, kMultiVpt);
         if (!c->k) return SNR_ERR_SHAPE;
         c->chunks = split_chunks(c->k, nv);
@@ -265,7 +392,10 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
     // -> 2.93), whose first phase also stores the sum. What helps is leaving
     // the 16-wavefront workgroup: halving 512 x 2 into 256 x 4 was 5-15%
     // slower for every operation (one row of 4096: tail 2.68 -> 2.85 us).
-    if (st == ST_F32 && op != OP_ADD_NORM && best->g == 1024 &&
+    // RMSNorm into Q8_1 records was not measured this way and keeps its
+    // tile.
+    if (st == ST_F32 && op != OP_ADD_NORM && op != OP_NORM_Q8 &&
+        best->g == 1024 &&
         best->vpt == 2 && rows > 0 && rows <= kEarlyBlocks) {
         const KernelEntry *half = find_entry(op, st, w, KIND_ROWTILE, 512, 4);
         if (half && 512LL * 4 >= nv) best = half;
@@ -368,47 +498,76 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             hipError_t e = k->rowtile(a, r0, nr, stream);
             if (e != hipSuccess) return hip_fail(e);
         }
-    } else if (k->kind == KIND_MULTIPASS) {
-        Workspace ws;
-        rc = get_workspace(dev, stream, &ws);
-        if (rc != SNR_OK) return rc;
-        // partial sums (rows x chunks) and inverse norms (rows) must fit the
-        // scratch; each pass's grid (rows x chunks workgroups) must fit a
-        // launch
-        int64_t step = kMultiFloats / (c.chunks + 1);
-        const int64_t max_grid = (int64_t)(UINT32_MAX / (uint32_t)k->block);
-        if (step * c.chunks > max_grid) step = max_grid / c.chunks;
-        if (step < 1) return SNR_ERR_SHAPE;
-        for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
-            const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
-            hipError_t e = k->multipass(a, ws.multi, r0, nr, c.chunks, stream);
-            if (e != hipSuccess) return hip_fail(e);
-        }
     } else {
-        int per_cu = 0;
-        hipError_t e = k->occupancy(&per_cu);
-        if (e != hipSuccess) return hip_fail(e);
-        // Every workgroup of the cooperative grid must be co-resident: at
-        // most floor(capacity / chunks) rows are in flight at once.
-        const int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
-        if (max_groups < 1) return SNR_ERR_WORKSPACE;
-        Workspace w_all;
-        rc = get_workspace(dev, stream, &w_all);
+        // Split-row and multi-pass launches use a workspace: the whole
+        // sequence is enqueued under the workspace lock, after the wait on
+        // its previous use and before the record of this one.
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        Workspace *ws = nullptr;
+        bool eager = true;
+        rc = acquire_workspace(dev, stream, &ws, &eager);
         if (rc != SNR_OK) return rc;
-        SplitState ws = w_all.st;
-        // Test hook: a small poll budget forces the bounded-wait path.
-        if (const char *lim = std::getenv("SNR_SPLIT_SPIN_LIMIT")) {
-            const long v = std::strtol(lim, nullptr, 10);
-            if (v > 0) ws.spin_limit = (uint32_t)v;
-        }
-        int64_t step = kSlotCap / c.chunks;
-        if (step > kRowCap) step = kRowCap;
-        for (int64_t r0 = 0; r0 < a.rows; r0 += step) {
-            const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
-            const int groups = (int)(nr < max_groups ? nr : max_groups);
-            e = k->split(a, ws, r0, nr, c.chunks, groups, stream);
+        if (eager) {
+            hipError_t e = hipStreamWaitEvent(stream, ws->last_use, 0);
             if (e != hipSuccess) return hip_fail(e);
         }
+        hipError_t e = hipSuccess;
+        if (k->kind == KIND_MULTIPASS) {
+            // partial sums (rows x chunks) and inverse norms (rows) must fit
+            // the scratch; each pass's grid (rows x chunks workgroups) must
+            // fit a launch
+            int64_t step = kMultiFloats / (c.chunks + 1);
+            const int64_t max_grid = (int64_t)(UINT32_MAX / (uint32_t)k->block);
+            if (step * c.chunks > max_grid) step = max_grid / c.chunks;
+            if (step < 1) return SNR_ERR_SHAPE;
+            float *scratch = multi_scratch(ws->base);
+            for (int64_t r0 = 0; r0 < a.rows && e == hipSuccess; r0 += step) {
+                const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
+                e = k->multipass(a, scratch, r0, nr, c.chunks, stream);
+            }
+        } else {
+            int per_cu = 0;
+            e = k->occupancy(&per_cu);
+            if (e != hipSuccess) return hip_fail(e);
+            // Every workgroup of the grid must be resident at once: at most
+            // floor(capacity / chunks) rows are in flight.
+            const int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
+            if (max_groups < 1) return SNR_ERR_WORKSPACE;
+            const SplitState st = split_state(ws->base);
+            // each launch's rows x reductions x chunks slots fit the slots
+            const int64_t nph = op == OP_TAIL ? 2 : 1;
+            const int64_t step = st.slot_cap / (c.chunks * nph);
+            if (step < 1) return SNR_ERR_SHAPE;
+            // Split-row launches never overlap one another on a device, on
+            // any stream: two grids that each fill the device could then
+            // each be partly resident, waiting for workgroups the other
+            // keeps out. (Under capture the graph's stream order is the
+            // caller's to keep.)
+            hipEvent_t *prev = nullptr;
+            if (eager) {
+                rc = split_serial_event(dev, &prev);
+                if (rc != SNR_OK) return rc;
+                e = hipStreamWaitEvent(stream, *prev, 0);
+                if (e != hipSuccess) return hip_fail(e);
+            }
+            const bool coop = split_cooperative();
+            for (int64_t r0 = 0; r0 < a.rows && e == hipSuccess; r0 += step) {
+                const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
+                const int groups = (int)(nr < max_groups ? nr : max_groups);
+                SplitState sl = st;
+                e = take_tag(ws, st.slots, eager, stream, &sl.tag);
+                // a replay repeats the captured tag: clear the slots this
+                // launch uses first (a kernel, recorded with it)
+                if (e == hipSuccess && !eager)
+                    e = fill_words(st.slots, nr * nph * c.chunks * 2, 0u,
+                                   stream);
+                if (e == hipSuccess)
+                    e = k->split(a, sl, r0, nr, c.chunks, groups, coop, stream);
+            }
+            if (e == hipSuccess && eager) e = hipEventRecord(*prev, stream);
+        }
+        if (e == hipSuccess && eager) e = hipEventRecord(ws->last_use, stream);
+        if (e != hipSuccess) return hip_fail(e);
     }
     if (k->kind == KIND_ROWTILE || k->kind == KIND_PERSIST)
         std::snprintf(t_last_shape, sizeof t_last_shape, "%s:%d:%d:%d",
@@ -719,12 +878,16 @@ const char *snr_strerror(int code) {
     case SNR_ERR_ALIAS: return "output buffers overlap inputs or each other";
     case SNR_ERR_ALIGN: return "pointer not aligned to its element size";
     case SNR_ERR_WORKSPACE:
-        return "split-row workspace unavailable or row too wide for "
-               "co-resident workgroups";
+        return "workspace unavailable (allocation failed or every workspace "
+               "held by a captured graph), or a forced split shape whose "
+               "chunks cannot all be co-resident";
     case SNR_ERR_HIP: return "HIP runtime call failed";
     case SNR_ERR_DEVICE:
         return "current device is not a gfx950 GPU, or the stream belongs to "
                "another device";
+    case SNR_ERR_CAPTURE:
+        return "rows wider than 65536 elements under graph capture need a "
+               "workspace: make one such call on the stream before capturing";
     default: return "unknown error code";
     }
 }
@@ -754,25 +917,29 @@ int snr_split_timeouts(hipStream_t stream, int64_t *count) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
-    Workspace w;
-    {
-        std::lock_guard<std::mutex> lk(g_ws_mu);
-        auto it = g_ws.find(std::make_pair(dev, stream));
-        if (it == g_ws.end()) return SNR_OK;
-        w = it->second;
-    }
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e);
-    unsigned int host = 0;
-    e = hipMemcpy(&host, w.st.timeouts, sizeof host, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e);
-    *count = host;
-    if (host != 0) {
-        // A wait that gave up may leave published slots behind: clear the
-        // whole workspace so the next launch starts from zero.
-        e = zero_words(w.base, w.words, stream);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find(dev);
+    if (it == g_ws.end()) return SNR_OK;
+    for (Workspace &w : it->second) {
+        if (w.stream != stream) continue;
+        // every eager use of the workspace is recorded in last_use; graph
+        // replays on the stream are covered by synchronising it
+        e = hipEventSynchronize(w.last_use);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e);
+        unsigned int *word = split_state(w.base).hdr + kHdrTimeouts;
+        unsigned int host = 0;
+        e = hipMemcpy(&host, word, sizeof host, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e);
+        *count = host;
+        if (host != 0) {
+            // Tags keep later launches from taking anything left behind by
+            // a wait that gave up, so only the count is reset.
+            static const unsigned int zero = 0;
+            e = hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        break;
     }
     return SNR_OK;
 }

@@ -61,32 +61,34 @@ struct MultiArgs {
     int32_t rem;
 };
 
-// Cross-workgroup state of the split-row kernels (device memory, owned by a
-// per-(device, stream) workspace). Every field starts at zero and every
-// launch leaves it at zero again (see the split kernel).
+// Cross-workgroup state of a split-row launch (see snr_split.hip for the
+// protocol): slots[] in a workspace's device memory holds one tagged partial
+// sum per (row of a launch, reduction, chunk); hdr[kHdrTimeouts] counts the
+// waits that gave up; `tag` is the launch's tag (never 0).
+constexpr int kHdrTimeouts = 0;
 struct SplitState {
-    unsigned long long *slots;  // [2][slot_cap] published partial sums
-    unsigned int *depart;       // [2][row_cap] readers done per row
-    unsigned int *timeouts;     // bounded-wait overruns (watchdog count)
-    int64_t slot_cap;           // capacity of one slot set
-    int64_t row_cap;            // capacity of one depart set
+    unsigned long long *slots;  // [slot_cap] (tag << 32) | f32 partial
+    unsigned int *hdr;          // hdr[kHdrTimeouts]: wait overruns
+    int64_t slot_cap;           // slots available to one launch
     uint32_t spin_limit;        // polls before a wait gives up
+    uint32_t tag;               // this launch's tag
 };
 
 // Row-tile launches of at most this many workgroups load the gains with the
 // row (one memory round trip fewer per step; slower over many rows).
 constexpr int64_t kEarlyBlocks = 16;
 
-// Chunk geometry of the split-row kernels: 256 threads per workgroup, each
-// holding `vpt` loads of the chunk.
+// Chunk geometry of the split-row kernels: 256 threads per workgroup and
+// 4096 elements per chunk (4 vectors per lane in f32, 2 in 16-bit storage).
 constexpr int kSplitBlock = 256;
+constexpr int kSplitChunkElems = 4096;
 constexpr int kSplitMaxChunks = 1024;
 
 using RowtileLaunch = hipError_t (*)(const RowArgs &, int64_t row0,
                                      int64_t nrows, hipStream_t);
 using SplitLaunch = hipError_t (*)(const RowArgs &, const SplitState &,
                                    int64_t row0, int64_t nrows, int chunks,
-                                   int groups, hipStream_t);
+                                   int groups, bool cooperative, hipStream_t);
 using OccupancyQuery = hipError_t (*)(int *blocks_per_cu);
 // Workgroups the current device holds at once (cached; 0 when unknown).
 using ResidentQuery = int64_t (*)();
@@ -96,9 +98,10 @@ using MultipassLaunch = hipError_t (*)(const RowArgs &, float *scratch,
                                        int64_t row0, int64_t nrows,
                                        int chunks, hipStream_t);
 
-// Geometry of the multi-pass kernels: 256 threads x 8 vectors per chunk.
+// Geometry of the multi-pass kernels: 256 threads x 16 vectors per chunk
+// (16384 f32 or 32768 16-bit elements).
 constexpr int kMultiBlock = 256;
-constexpr int kMultiVpt = 8;
+constexpr int kMultiVpt = 16;
 
 struct KernelEntry {
     int op;        // Op
@@ -121,9 +124,11 @@ struct KernelEntry {
 const KernelEntry *kernel_table(int *count);
 const KernelEntry *q8_kernel_table(int *count);
 const KernelEntry *persist_kernel_table(int *count);   // snr_persist.hip
+const KernelEntry *split_kernel_table(int *count);     // snr_split.hip
 
-// Zero `words` 32-bit words with a kernel (used instead of a memset so that
-// the call can also be recorded into a HIP graph).
-hipError_t zero_words(void *p, int64_t words, hipStream_t stream);
+// Set `words` 32-bit words to `value` with a kernel (used instead of a
+// memset so that the call can also be recorded into a HIP graph).
+hipError_t fill_words(void *p, int64_t words, unsigned int value,
+                      hipStream_t stream);
 
 }  // namespace snr

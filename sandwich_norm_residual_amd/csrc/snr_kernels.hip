@@ -32,14 +32,8 @@
 // * Row-tile kernel: G lanes per row. G <= 64 packs 64/G rows into each
 //   wavefront (small rows, no LDS and no barrier); G > 64 spans G/64
 //   wavefronts of one workgroup.
-// * Split-row kernel for very wide rows: one workgroup per chunk of a row. A
-//   workgroup publishes its chunk's partial sum to device memory, waits for
-//   the other chunks of its row, adds the partials in chunk order and
-//   normalises its chunk from registers (no second read of the row). The
-//   grid is a cooperative launch (every workgroup co-resident) of `groups`
-//   x `chunks` workgroups; workgroup (g, c) handles chunk c of rows g,
-//   g + groups, g + 2 groups, ... in order, so a wait only ever depends on
-//   resident workgroups that are working on the same row.
+// * Split-row kernels for very wide rows (one workgroup per chunk of a row,
+//   partial sums combined through device memory) are in snr_split.hip.
 // * Multi-pass kernels for rows so wide that their chunks cannot all be
 //   co-resident: partial sums through device memory (rows read twice).
 // * Stores of outputs and loads of row data are non-temporal (each byte is
@@ -50,7 +44,7 @@ namespace snr {
 namespace {
 
 // ---------------------------------------------------------------------------
-// One row (or one chunk of a row), shared by the row-tile and split kernels.
+// One row, shared by the row-tile and several-segment kernels.
 //
 // The lane holds vectors vbase + k*vstride (k < VPT) of the row and, when
 // `sown`, the remainder elements sbase + q*sstride (q < EX) that follow the
@@ -355,97 +349,6 @@ multi_kernel(MultiArgs m, int64_t row0, int64_t row_end) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-row kernel: chunk c of rows g, g + groups, ... for workgroup
-// (g, c) of a cooperative grid of groups x chunks workgroups.
-// ---------------------------------------------------------------------------
-constexpr int SB = kSplitBlock;   // SNW = SB / 64 wavefronts (snr_device.h)
-
-// Publish this chunk's partial, gather the partials of every chunk of the
-// row in chunk order, and leave the row's slots at zero once every chunk has
-// read them. `set` selects one of two independent slot sets (the tail's two
-// reductions). Each slot is one 64-bit word (flag in the high half, the f32
-// partial in the low half), so no fence is needed between value and flag.
-__device__ float cross_chunk_total(float partial, const SplitState &st,
-                                   int set, int64_t row_local, int chunk,
-                                   int chunks, float *part) {
-    const int tid = threadIdx.x;
-    unsigned long long *slots = st.slots + set * st.slot_cap +
-                                row_local * (int64_t)chunks;
-    unsigned int *depart = st.depart + set * st.row_cap + row_local;
-    if (tid == 0) {
-        const unsigned long long word =
-            (1ull << 32) | (unsigned long long)__float_as_uint(partial);
-        __hip_atomic_store(slots + chunk, word, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    for (int j = tid; j < chunks; j += SB) {
-        unsigned long long v;
-        uint32_t polls = 0;
-        while (((v = __hip_atomic_load(slots + j, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0) {
-            if (++polls >= st.spin_limit) {
-                __hip_atomic_fetch_add(st.timeouts, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        part[j] = __uint_as_float((unsigned int)v);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned int done = __hip_atomic_fetch_add(
-            depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == (unsigned int)chunks - 1) {
-            for (int j = 0; j < chunks; ++j)
-                __hip_atomic_store(slots + j, 0ull, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    // In chunk order, in blocks of 32: a chain of at most 32 + 31 additions
-    // instead of `chunks` (equal partials, as a constant row gives, drift by
-    // about one rounding per addition in a single chain). Every lane adds in
-    // the same order, so all get the same bits.
-    float t = 0.0f;
-    for (int b = 0; b < chunks; b += 32) {
-        const int e = b + 32 < chunks ? b + 32 : chunks;
-        float s = part[b];
-        for (int j = b + 1; j < e; ++j) s += part[j];
-        t = b == 0 ? s : t + s;
-    }
-    return t;
-}
-
-template <int OP, int ST, int VPT>
-__global__ void __launch_bounds__(SB)
-split_kernel(RowArgs p, SplitState st, int64_t row0, int64_t nrows,
-             int chunks, int groups) {
-    __shared__ float red[2][SNW];
-    __shared__ float part[kSplitMaxChunks];
-
-    const int tid = threadIdx.x;
-    const int chunk = (int)(blockIdx.x % (unsigned)chunks);
-    const int group = (int)(blockIdx.x / (unsigned)chunks);
-    const int vbase = chunk * (SB * VPT) + tid;
-    const bool last = chunk == chunks - 1;  // the last chunk owns the remainder
-
-    for (int64_t rl = group; rl < nrows; rl += groups) {
-        const int64_t off = (row0 + rl) * (int64_t)p.n;
-        process_row<OP, ST, VPT, 1, false, false>(
-            p, off, true, vbase, SB, tid, SB, last,
-            [&](float s, int which) {
-                return cross_chunk_total(block_total(s, red[which]), st, which,
-                                         rl, chunk, chunks, part);
-            });
-        // The next row rewrites `part` and `red`: every lane must have
-        // finished reading them first.
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Multi-pass kernels for rows too wide to keep on chip (more chunks than
 // co-resident workgroups). Each pass is a plain grid; partial sums go
 // through device memory and are added in chunk order, so results stay
@@ -540,11 +443,11 @@ pass_fuse(RowArgs p, int64_t row0, int chunks, const float *inv, float *part) {
     }
 }
 
-__global__ void zero_kernel(unsigned int *p, int64_t words) {
+__global__ void fill_kernel(unsigned int *p, int64_t words, unsigned int v) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
          i < words; i += stride)
-        p[i] = 0u;
+        p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -617,25 +520,6 @@ constexpr MultiLaunch multi_for() {
     else return nullptr;
 }
 
-template <int OP, int ST, int VPT>
-hipError_t launch_split(const RowArgs &p, const SplitState &st, int64_t row0,
-                        int64_t nrows, int chunks, int groups,
-                        hipStream_t stream) {
-    RowArgs pa = p;
-    SplitState sa = st;
-    int c = chunks, g = groups;
-    void *args[] = {&pa, &sa, &row0, &nrows, &c, &g};
-    return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&split_kernel<OP, ST, VPT>),
-        dim3((unsigned int)(groups * chunks)), dim3(SB), args, 0, stream);
-}
-
-template <int OP, int ST, int VPT>
-hipError_t occupancy_split(int *blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, split_kernel<OP, ST, VPT>, SB, 0);
-}
-
 // Multi-pass launch over rows [row0, row0 + nrows): scratch holds
 // nrows * chunks partial sums followed by nrows inverse norms.
 template <int OP, int ST>
@@ -687,10 +571,6 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 #define SNR_RT(OP, ST, G, VPT) SNR_RT_M(OP, ST, G, VPT, nullptr)
 #define SNR_RT_A(OP, ST, G, VPT)                                            \
     SNR_RT_M(OP, ST, G, VPT, (multi_for<OP, ST, G, VPT>()))
-#define SNR_SPLIT(OP, ST)                                                   \
-    KernelEntry{OP, ST, Codec<ST>::W, KIND_SPLIT, SB, 8, SB, nullptr,        \
-                &launch_split<OP, ST, 8>, &occupancy_split<OP, ST, 8>,      \
-                nullptr, nullptr}
 #define SNR_MULTI(OP, ST)                                                   \
     KernelEntry{OP, ST, Codec<ST>::W, KIND_MULTIPASS, MB, MVPT, MB, nullptr, \
                 nullptr, nullptr, &launch_multipass<OP, ST>, nullptr}
@@ -699,7 +579,8 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
 // sub-wavefront groups with 4 vectors per lane, then one row per workgroup
 // with the smallest register tile that holds about two vectors per lane
 // (registers are allocated for every slot of a tile, used or not, and
-// occupancy follows them), then split and multi-pass.
+// occupancy follows them), then multi-pass (the split-row kernels have a
+// table of their own, snr_split.hip).
 #define SNR_AUTO_SHAPES(OP, ST)                                             \
     SNR_RT_A(OP, ST, 1, 4), SNR_RT_A(OP, ST, 2, 4), SNR_RT_A(OP, ST, 4, 4), \
     SNR_RT_A(OP, ST, 8, 4), SNR_RT_A(OP, ST, 16, 4),                        \
@@ -708,7 +589,7 @@ hipError_t launch_multipass(const RowArgs &p, float *scratch, int64_t row0,
     SNR_RT_A(OP, ST, 256, 4), SNR_RT_A(OP, ST, 512, 2),                     \
     SNR_RT_A(OP, ST, 512, 4), SNR_RT_A(OP, ST, 1024, 1),                    \
     SNR_RT_A(OP, ST, 1024, 2), SNR_RT_A(OP, ST, 1024, 4),                   \
-    SNR_RT_A(OP, ST, 1024, 8), SNR_SPLIT(OP, ST), SNR_MULTI(OP, ST)
+    SNR_RT_A(OP, ST, 1024, 8), SNR_MULTI(OP, ST)
 
 // Further shapes, reachable only by forcing (shape sweeps and tests).
 #define SNR_SWEEP_SHAPES(OP, ST)                                            \
@@ -741,12 +622,13 @@ const KernelEntry *kernel_table(int *count) {
     return kTable;
 }
 
-hipError_t zero_words(void *p, int64_t words, hipStream_t stream) {
+hipError_t fill_words(void *p, int64_t words, unsigned int value,
+                      hipStream_t stream) {
     if (words <= 0) return hipSuccess;
     int64_t blocks = (words + 255) / 256;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned int)blocks), dim3(256), 0,
-                       stream, static_cast<unsigned int *>(p), words);
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned int)blocks), dim3(256), 0,
+                       stream, static_cast<unsigned int *>(p), words, value);
     return hipGetLastError();
 }
 

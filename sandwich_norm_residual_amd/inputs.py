@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for RMSNorm and the dual-epsilon sandwich tail.
 
 This module is shared by the GPU path's tests and benchmark and by the oracle's
-tests. It draws random numbers and lays out arrays; it contains none of the
-method's arithmetic (no mean of squares, no epsilon, no normalisation).
+tests. It draws random numbers, lays out arrays, and scales each edge-sweep
+row to its drawn target mean square (the input recipe); it contains none of
+the method's arithmetic (no epsilon, no normalised output, no gain applied).
 
 The workloads stand in for the residual stream of the model the Muser book
 describes (hidden width n = 6656, section 12.1 of "RMSNorm and the
@@ -145,6 +146,16 @@ def _configs() -> dict:
     for n in EDGE_NS:
         add(Config(f"edge_256x{n}_f32", "plain", 256, n, "f32", 500 + n,
                    (1e-5,), ((-12.0, 6.0),), edge=True))
+    # rows wider than any register tile (65536 elements): the split-row
+    # kernels, with the plain norm's and the tail's recipes
+    add(Config("plain_256x262144_f32", "plain", 256, 262144, "f32", 351,
+               (1e-5,), ((-2.0, 1.0),)))
+    add(Config("tail_256x262144_f32", "tail", 256, 262144, "f32", 352,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
+    add(Config("plain_16x1048576_f32", "plain", 16, 1048576, "f32", 353,
+               (1e-5,), ((-2.0, 1.0),)))
+    add(Config("tail_16x1048576_f32", "tail", 16, 1048576, "f32", 354,
+               (EPS_POST, EPS_PRE), ((-3.0, 2.0), (-1.0, 1.0))))
     return c
 
 
@@ -164,14 +175,17 @@ def _scaled_normal(rng, rows, n, lo, hi) -> np.ndarray:
     return z.astype(F32)
 
 
-def _edge_rows(rng, rows, n, lo, hi) -> np.ndarray:
-    """Edge-sweep rows: row i has target mean-square m_i = 10**U(lo, hi), drawn
-    as N(0,1) * sqrt(m_i) (so E[mean(x^2)] = m_i). Rows 0-5 are structured:
-    all zero, constant +c, constant -c, alternating +-c, a one-hot spike, and a
-    row at the smallest target mean-square 10**lo."""
+def _edge_rows(rng, rows, n, lo, hi):
+    """Edge-sweep rows and their target mean squares: row i has target
+    mean-square m_i = 10**U(lo, hi) and is z * sqrt(m_i / mean(z^2)) with z
+    drawn N(0,1), so its mean square is m_i up to the final rounding to f32.
+    Rows 0-5 are structured (their targets are not used): all zero, constant
+    +c, constant -c, alternating +-c, a one-hot spike, and a row at the
+    smallest target mean-square 10**lo."""
     m = 10.0 ** rng.uniform(lo, hi, rows)
     z = rng.standard_normal((rows, n))
-    z *= np.sqrt(m)[:, None]
+    ms = np.mean(z * z, axis=1)
+    z *= np.sqrt(m / ms)[:, None]
     x = z.astype(F32)
     c = 1.5
     if rows > 0:
@@ -186,8 +200,9 @@ def _edge_rows(rng, rows, n, lo, hi) -> np.ndarray:
         x[4] = 0.0
         x[4, n // 2] = 100.0
     if rows > 5:
-        x[5] = (rng.standard_normal(n) * np.sqrt(10.0 ** lo)).astype(F32)
-    return x
+        z5 = rng.standard_normal(n)
+        x[5] = (z5 * np.sqrt(10.0 ** lo / np.mean(z5 * z5))).astype(F32)
+    return x, m
 
 
 def make_plain(cfg: Config, rows: int | None = None) -> dict:
@@ -199,12 +214,15 @@ def make_plain(cfg: Config, rows: int | None = None) -> dict:
     rng = rng_for(cfg.seed)
     gamma = _gamma(rng, cfg.n)
     lo, hi = cfg.scale_exp[0]
+    out = {}
     if cfg.edge:
-        x = _edge_rows(rng, rows, cfg.n, lo, hi)
+        x, out["target_ms"] = _edge_rows(rng, rows, cfg.n, lo, hi)
     else:
         x = _scaled_normal(rng, rows, cfg.n, lo, hi)
-    return {"x": to_storage(x, cfg.dtype), "gamma": to_storage(gamma, cfg.dtype),
-            "eps": cfg.eps[0], "dtype": cfg.dtype}
+    out.update({"x": to_storage(x, cfg.dtype),
+                "gamma": to_storage(gamma, cfg.dtype), "eps": cfg.eps[0],
+                "dtype": cfg.dtype})
+    return out
 
 
 def make_tail(cfg: Config, rows: int | None = None) -> dict:

@@ -56,6 +56,7 @@ def test_error_codes_match_header():
     for name in ["SNR_OK", "SNR_ERR_NULL", "SNR_ERR_SHAPE", "SNR_ERR_DTYPE",
                  "SNR_ERR_EPS", "SNR_ERR_ALIAS", "SNR_ERR_ALIGN",
                  "SNR_ERR_WORKSPACE", "SNR_ERR_HIP", "SNR_ERR_DEVICE",
+                 "SNR_ERR_CAPTURE",
                  "SNR_F32", "SNR_BF16", "SNR_F16"]:
         assert header_enum(name) == getattr(_lib, name), name
     assert header_enum("SNR_SHAPE_ROWTILE") == _lib.SHAPE_ROWTILE
@@ -65,11 +66,11 @@ def test_error_codes_match_header():
 
 def test_strerror_covers_every_code(L):
     seen = set()
-    for code in range(10):
+    for code in range(11):
         text = _lib.strerror(code)
         assert text and text != "unknown error code", code
         seen.add(text)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert _lib.strerror(12345) == "unknown error code"
 
 

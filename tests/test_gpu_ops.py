@@ -75,8 +75,10 @@ def test_forced_shape(oracle, case):
     w = VEC[st]
     if kind == "rowtile":
         nv = max(1, g * v - g // 2 - (1 if g == 1 else 0))
+    elif kind == "split":
+        nv = 2 * (4096 // w) + 5   # three chunks of 4096 elements
     else:
-        nv = 2 * 2048 + 5          # three chunks of 256 x 8 vectors
+        nv = 2 * 4096 + 5          # three chunks of 256 x 16 vectors
     n = nv * w + w - 1
     rows = 19
     label = f"{op}-{st}-{kind}-g{g}-v{v}-n{n}"
@@ -87,8 +89,10 @@ def test_forced_shape(oracle, case):
                               scale=1.5 if op == "norm_add" else None)
     if kind == "rowtile":
         assert shape == f"rowtile:{g}:{v}:{w}", shape
+    elif kind == "split":
+        assert shape == f"split:256:{4096 // (256 * w)}:{w}:3", shape
     else:
-        assert shape.startswith(f"{kind}:256:8:{w}:3"), shape
+        assert shape == f"multipass:256:16:{w}:3", shape
 
 
 @pytest.mark.parametrize("name", ["tail_4096x6656_bf16", "tail_4096x6656_f16",

@@ -95,8 +95,8 @@ def test_forced_rowtile_shape(oracle, case):
 
 @pytest.mark.parametrize("op", ["plain", "tail"])
 @pytest.mark.parametrize("ragged", [False, True])
-@pytest.mark.parametrize("chunks_nv", [(1, 0), (1, 100), (3, 2 * 2048 + 5),
-                                       (5, 5 * 2048)])
+@pytest.mark.parametrize("chunks_nv", [(1, 0), (1, 100), (3, 2 * 1024 + 5),
+                                       (5, 5 * 1024)])
 def test_forced_split(oracle, op, ragged, chunks_nv):
     chunks, nv = chunks_nv
     n = nv * 4 + (3 if ragged else 0)
@@ -116,7 +116,7 @@ def test_forced_split(oracle, op, ragged, chunks_nv):
             h, y = run_tail(inp)
             shape = snr.last_shape()
             check_tail(oracle, inp, h, y, f"split-{op}-n{n}")
-    assert shape == f"split:256:8:4:{chunks}", shape
+    assert shape == f"split:256:4:4:{chunks}", shape
     assert snr.split_timeouts() == 0
 
 
@@ -131,7 +131,7 @@ def test_split_full_size(oracle, name):
         got, _ = run_plain(inp)
         shape = snr.last_shape()
     check_plain(oracle, inp, got, f"split-{name}")
-    assert shape.startswith("split:256:8:4:")
+    assert shape.startswith("split:256:4:4:")
     tin = gen.random_tail(64, cfg.n, 9100 + cfg.n)
     with snr.forced_shape("split", 0, 8):
         h, y = run_tail(tin)
@@ -146,7 +146,7 @@ def test_forced_multipass(oracle, op_st, n):
     op, st = op_st
     w = VEC[st]
     rows = 7
-    chunks = max(1, -(-(n // w) // 2048))
+    chunks = max(1, -(-(n // w) // 4096))
     say(f"forced multipass {op} {st} rows={rows} n={n}")
     with snr.forced_shape("multipass"):
         if op == "plain":
@@ -159,7 +159,7 @@ def test_forced_multipass(oracle, op_st, n):
             h, y = run_tail(inp)
             shape = snr.last_shape()
             check_tail(oracle, inp, h, y, f"multipass-tail-{n}")
-    assert shape == f"multipass:256:8:{w}:{chunks}", shape
+    assert shape == f"multipass:256:16:{w}:{chunks}", shape
 
 
 @pytest.mark.parametrize("op_st_n", [("plain", "f32", 8192 * 1024 + 5),
@@ -181,7 +181,7 @@ def test_rows_wider_than_the_split_capacity(oracle, op_st_n):
         h, y = run_tail(inp)
         shape = snr.last_shape()
         check_tail(oracle, inp, h, y, "wide-tail")
-    assert shape.startswith("multipass:256:8:"), shape
+    assert shape.startswith("multipass:256:16:"), shape
 
 
 def test_forced_shape_that_cannot_hold_the_row_is_refused():
@@ -298,7 +298,7 @@ def test_bitwise_deterministic(name):
 
 @pytest.mark.parametrize("op,rows,n", [("plain", 1024, 65536),
                                         ("tail", 512, 65536),
-                                        ("plain", 2000, 3 * 2048 * 4 + 5)])
+                                        ("plain", 2000, 3 * 1024 * 4 + 5)])
 def test_split_repeated_runs_are_identical(oracle, op, rows, n):
     """The split-row kernel is the one path whose workgroups wait on one
     another. With more rows than can be co-resident (each workgroup walks
@@ -329,7 +329,7 @@ def test_split_repeated_runs_are_identical(oracle, op, rows, n):
             torch.cuda.synchronize()
             for o, f in zip(outs, first):
                 assert torch.equal(o, f)
-    assert shape.startswith("split:256:8:4:"), shape
+    assert shape.startswith("split:256:4:4:"), shape
     assert snr.split_timeouts() == 0
     if op == "plain":
         check_plain(oracle, inp, host_f64(first[0]), f"split-repeat-{n}")
@@ -368,17 +368,17 @@ def test_subnormal_epsilon(oracle, n):
     assert not h[1].any() and not y[1].any()
 
 
-@pytest.mark.parametrize("shape,n,op", [("split", 8192 * 1024, "plain"),
-                                        ("split", 700 * 8192, "tail"),
-                                        ("multipass", 8192 * 1024, "plain"),
+@pytest.mark.parametrize("shape,n,op", [("split", 4096 * 1024, "plain"),
+                                        ("split", 700 * 4096, "tail"),
+                                        ("multipass", 16384 * 1024, "plain"),
                                         ("multipass", 4 * 8192 * 1024 + 5,
                                          "plain")])
 def test_wide_constant_rows(oracle, shape, n, op):
-    """Constant rows cut into 700 to 1024 chunks (4097 per row on the
-    multi-pass path): every chunk's partial sum of squares is the same,
-    which is where adding the partials in one chain drifts by about a
-    rounding per addition (1e-5 of the sum at 1024 chunks). Added in blocks
-    of 32 they stay within 2e-6 of the exact result."""
+    """Constant rows cut into 700 to 2049 chunks: every chunk's partial sum
+    of squares is the same, which is where adding the partials in one chain
+    drifts by about a rounding per addition (1e-5 of the sum at 1024
+    chunks). Added in blocks of 32 they stay within 2e-6 of the exact
+    result."""
     say(f"wide constant rows {shape} {op} n={n}")
     rows = 2
     if op == "plain":
@@ -456,16 +456,17 @@ def test_bf16_output_is_round_to_nearest_even(oracle):
 
 def test_split_wait_budget_exhausted_is_reported_and_recovered(oracle,
                                                               monkeypatch):
-    """Force the split-row kernel's bounded wait to give up (a budget of one
-    poll): the kernel still finishes, the overrun is counted, and the next
-    call with the normal budget is correct again."""
+    """Force the split-row kernel's bounded wait to give up (a budget of no
+    polls): the kernel still finishes, its outputs are NaN, the overrun is
+    counted, and the next call with the normal budget is correct again."""
     rows, n = 64, 5 * 2048 * 4
     say(f"split watchdog rows={rows} n={n}")
     inp = gen.random_plain(rows, n, 4242)
     assert snr.split_timeouts() == 0
-    monkeypatch.setenv("SNR_SPLIT_SPIN_LIMIT", "1")
+    monkeypatch.setenv("SNR_SPLIT_SPIN_LIMIT", "0")
     with snr.forced_shape("split", 0, 8):
-        run_plain(inp)
+        bad, _ = run_plain(inp)
+        assert np.isnan(bad).all()
         assert snr.split_timeouts() > 0
         monkeypatch.delenv("SNR_SPLIT_SPIN_LIMIT")
         got, _ = run_plain(inp)

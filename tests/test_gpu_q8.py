@@ -43,7 +43,7 @@ def test_forced_shape(oracle, case):
     if kind == "rowtile":
         nv = max(bv, (g * v - g // 2) // bv * bv)
     else:
-        nv = 2 * 2048 + 8          # three chunks of 256 x 8 vectors
+        nv = 2 * 4096 + 8          # three chunks of 256 x 16 vectors
     n = nv * w
     rows = 19
     label = f"q8-{st}-{kind}-g{g}-v{v}-n{n}"
@@ -56,7 +56,7 @@ def test_forced_shape(oracle, case):
     if kind == "rowtile":
         assert shape == f"rowtile:{g}:{v}:{w}", shape
     else:
-        assert shape.startswith(f"multipass:256:8:{w}:3"), shape
+        assert shape == f"multipass:256:16:{w}:3", shape
 
 
 @pytest.mark.parametrize("name", ["q8_4096x6656_f32", "q8_4096x6656_bf16",

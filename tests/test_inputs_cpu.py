@@ -115,19 +115,27 @@ def test_edge_rows(n):
     spike[n // 2] = 100.0
     assert np.array_equal(x[4], spike)
     ms = np.mean(x * x, axis=1)
-    assert 1e-12 * 0.8 < ms[5] < 1e-12 * 1.2
+    # the tiny row sits at the smallest target mean square, up to rounding
+    assert abs(ms[5] / 1e-12 - 1.0) < 1e-6
     rest = ms[6:]
-    # target mean-square log-uniform over 1e-12 .. 1e6 (sampling slack for
-    # the mean of n squares of a normal)
-    assert np.all(rest > 1e-12 * 0.8) and np.all(rest < 1e6 * 1.2)
-    assert rest.min() < 1e-9 and rest.max() > 1e3
+    # every other row's realised mean square is its drawn target m (up to
+    # the rounding of its elements to f32), log-uniform over 1e-12 .. 1e6
+    m = d["target_ms"][6:]
+    assert np.all(np.abs(rest / m - 1.0) < 1e-6)
+    assert np.all(m >= 1e-12) and np.all(m <= 1e6)
+    assert m.min() < 1e-9 and m.max() > 1e3
 
 
 def test_small_edge_rows_keep_their_structure():
     for n in (2, 3):
-        x = gen.make(f"edge_256x{n}_f32")["x"]
+        d = gen.make(f"edge_256x{n}_f32")
+        x = d["x"]
         assert np.all(x[0] == 0) and np.all(x[1] == 1.5) and np.all(x[2] == -1.5)
         assert x[4, n // 2] == 100.0 and np.count_nonzero(x[4]) == 1
+        # even two or three elements carry the drawn mean square exactly
+        xd = x.astype(np.float64)
+        ms = np.mean(xd[6:] * xd[6:], axis=1)
+        assert np.all(np.abs(ms / d["target_ms"][6:] - 1.0) < 1e-6)
 
 
 def test_bf16_rounds_to_nearest_even():
