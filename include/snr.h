@@ -162,6 +162,34 @@ SNR_API int sandwich_tail(const float *a, const float *r, const float *gamma_pos
                   hipStream_t stream);
 
 /*
+ * sandwich_tail_noalloc - sandwich_tail for callers that cannot allocate
+ * device memory: code recorded into HIP graphs whose capture must not
+ * allocate, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as sandwich_tail (the same kernels, so
+ * the outputs are bit-identical). Where sandwich_tail would use an allocated
+ * workspace (rows wider than 65536 elements), this uses instead a 1 MiB
+ * array in the library's own device memory (a file-scope __device__ array;
+ * each GPU the library runs on holds one copy until the process ends). It
+ * calls no allocating routine. Rows are processed in batches sized to that
+ * array, so every row width the ABI accepts fits; a row that needed more
+ * would be refused with SNR_ERR_WORKSPACE.
+ *
+ * Every call on a GPU shares that GPU's array and no events order them:
+ * calls of this entry point that overlap on one GPU race (and so does one
+ * that overlaps another wide-row call there). Serialise them, e.g. on one
+ * stream. The array's slots carry per-call tags, so what an earlier call
+ * left there is never taken for a later call's. The first call on a device
+ * looks up the array's device address and clears it with a kernel on
+ * `stream`.
+ */
+SNR_API int sandwich_tail_noalloc(const float *a, const float *r,
+                                  const float *gamma_post, float eps_post,
+                                  const float *gamma_pre, float eps_pre,
+                                  float *h_out, float *y_out, int64_t rows,
+                                  int64_t n, hipStream_t stream);
+
+/*
  * sandwich_tail_typed - the same tail for any snr_dtype storage: a, r, both
  * gains, h_out and y_out all of type `dtype`. With bf16 or f16 storage, h is
  * stored rounded to the storage type, and y is the norm of its f32 value

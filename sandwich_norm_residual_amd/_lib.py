@@ -52,6 +52,8 @@ SIGNATURES = {
     "rmsnorm_fwd": (_int, [_vp, _vp, _f, _i64, _i64, _int, _vp, _vp]),
     "sandwich_tail": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp, _i64,
                              _i64, _vp]),
+    "sandwich_tail_noalloc": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp,
+                                     _i64, _i64, _vp]),
     "sandwich_tail_typed": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _vp,
                                    _i64, _i64, _int, _vp]),
     "sandwich_tail_inplace": (_int, [_vp, _vp, _vp, _f, _vp, _f, _vp, _i64,

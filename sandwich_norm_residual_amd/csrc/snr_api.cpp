@@ -452,10 +452,51 @@ int choose(int op, int st, int w, int64_t nv, int rem, int64_t rows,
 }
 
 // ---------------------------------------------------------------------------
+// The allocation-free entry point's scratch (sandwich_tail_noalloc): the
+// file-scope device array `scratch` (one copy per device, laid out as a
+// workspace), whose device address is looked up once per device at that
+// entry point's first call there. Its tag counter lives with the address.
+// ---------------------------------------------------------------------------
+constexpr int kMaxScratchDevices = 64;
+Workspace g_scratch_ws[kMaxScratchDevices];   // base == nullptr: not set up
+
+}  // namespace
+}  // namespace snr
+
+static __device__ __align__(256) unsigned char scratch[snr::kWorkspaceBytes];
+
+namespace snr {
+namespace {
+
+// The device address of `scratch` on device `dev`, cleared on `stream` the
+// first time (caller holds g_ws_mu; `dev` is the current device).
+int setup_scratch(int dev, hipStream_t stream) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return SNR_ERR_DEVICE;
+    Workspace &w = g_scratch_ws[dev];
+    if (w.base) return SNR_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    // the slots and the overrun count start at zero
+    e = fill_words(ptr, kWorkspaceBytes / 4, 0u, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    w.base = ptr;
+    w.next_tag = 1;
+    return SNR_OK;
+}
+
+int scratch_workspace(int dev, Workspace **out) {
+    if (dev < 0 || dev >= kMaxScratchDevices || !g_scratch_ws[dev].base)
+        return SNR_ERR_WORKSPACE;
+    *out = &g_scratch_ws[dev];
+    return SNR_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
 int launch(int op, int st, int64_t esize, const RowArgs &args_in,
-           hipStream_t stream) {
+           hipStream_t stream, bool use_scratch = false) {
     int dev = 0;
     DeviceInfo info;
     int rc = current_device(stream, &dev, &info);
@@ -502,12 +543,20 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         // Split-row and multi-pass launches use a workspace: the whole
         // sequence is enqueued under the workspace lock, after the wait on
         // its previous use and before the record of this one.
+        // The allocation-free entry point uses its device's static scratch
+        // instead, with no events (its calls must not overlap on a device).
         std::lock_guard<std::mutex> lk(g_ws_mu);
         Workspace *ws = nullptr;
-        bool eager = true;
-        rc = acquire_workspace(dev, stream, &ws, &eager);
+        bool eager = !capturing(stream);
+        bool events = false;
+        if (use_scratch) {
+            rc = scratch_workspace(dev, &ws);
+        } else {
+            rc = acquire_workspace(dev, stream, &ws, &eager);
+            events = eager;
+        }
         if (rc != SNR_OK) return rc;
-        if (eager) {
+        if (events) {
             hipError_t e = hipStreamWaitEvent(stream, ws->last_use, 0);
             if (e != hipSuccess) return hip_fail(e);
         }
@@ -519,7 +568,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             int64_t step = kMultiFloats / (c.chunks + 1);
             const int64_t max_grid = (int64_t)(UINT32_MAX / (uint32_t)k->block);
             if (step * c.chunks > max_grid) step = max_grid / c.chunks;
-            if (step < 1) return SNR_ERR_SHAPE;
+            if (step < 1) return use_scratch ? SNR_ERR_WORKSPACE : SNR_ERR_SHAPE;
             float *scratch = multi_scratch(ws->base);
             for (int64_t r0 = 0; r0 < a.rows && e == hipSuccess; r0 += step) {
                 const int64_t nr = a.rows - r0 < step ? a.rows - r0 : step;
@@ -537,14 +586,14 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             // each launch's rows x reductions x chunks slots fit the slots
             const int64_t nph = op == OP_TAIL ? 2 : 1;
             const int64_t step = st.slot_cap / (c.chunks * nph);
-            if (step < 1) return SNR_ERR_SHAPE;
+            if (step < 1) return use_scratch ? SNR_ERR_WORKSPACE : SNR_ERR_SHAPE;
             // Split-row launches never overlap one another on a device, on
             // any stream: two grids that each fill the device could then
             // each be partly resident, waiting for workgroups the other
             // keeps out. (Under capture the graph's stream order is the
             // caller's to keep.)
             hipEvent_t *prev = nullptr;
-            if (eager) {
+            if (events) {
                 rc = split_serial_event(dev, &prev);
                 if (rc != SNR_OK) return rc;
                 e = hipStreamWaitEvent(stream, *prev, 0);
@@ -564,9 +613,9 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
                 if (e == hipSuccess)
                     e = k->split(a, sl, r0, nr, c.chunks, groups, coop, stream);
             }
-            if (e == hipSuccess && eager) e = hipEventRecord(*prev, stream);
+            if (e == hipSuccess && events) e = hipEventRecord(*prev, stream);
         }
-        if (e == hipSuccess && eager) e = hipEventRecord(ws->last_use, stream);
+        if (e == hipSuccess && events) e = hipEventRecord(ws->last_use, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     if (k->kind == KIND_ROWTILE || k->kind == KIND_PERSIST)
@@ -619,7 +668,7 @@ int check_common(int64_t rows, int64_t n, int64_t es,
 int tail_impl(const void *a, const void *r, const void *gamma_post,
               float eps_post, const void *gamma_pre, float eps_pre,
               void *h_out, void *y_out, int64_t rows, int64_t n, int dtype,
-              hipStream_t stream) {
+              hipStream_t stream, bool use_scratch = false) {
     int64_t es = 0;
     const int st = storage_of(dtype, &es);
     if (st < 0) return SNR_ERR_DTYPE;
@@ -648,7 +697,16 @@ int tail_impl(const void *a, const void *r, const void *gamma_post,
     args.eps1 = eps_pre;
     args.rows = rows;
     args.n = (int32_t)n;
-    return launch(OP_TAIL, st, es, args, stream);
+    if (use_scratch) {
+        int dev = 0;
+        DeviceInfo info;
+        rc = current_device(stream, &dev, &info);
+        if (rc != SNR_OK) return rc;
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        rc = setup_scratch(dev, stream);
+        if (rc != SNR_OK) return rc;
+    }
+    return launch(OP_TAIL, st, es, args, stream, use_scratch);
 }
 
 }  // namespace
@@ -688,6 +746,15 @@ int sandwich_tail(const float *a, const float *r, const float *gamma_post,
                   hipStream_t stream) {
     return tail_impl(a, r, gamma_post, eps_post, gamma_pre, eps_pre, h_out,
                      y_out, rows, n, SNR_F32, stream);
+}
+
+int sandwich_tail_noalloc(const float *a, const float *r,
+                          const float *gamma_post, float eps_post,
+                          const float *gamma_pre, float eps_pre, float *h_out,
+                          float *y_out, int64_t rows, int64_t n,
+                          hipStream_t stream) {
+    return tail_impl(a, r, gamma_post, eps_post, gamma_pre, eps_pre, h_out,
+                     y_out, rows, n, SNR_F32, stream, true);
 }
 
 int sandwich_tail_typed(const void *a, const void *r, const void *gamma_post,
