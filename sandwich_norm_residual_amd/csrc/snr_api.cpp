@@ -105,6 +105,10 @@ constexpr int64_t kMultiOffset = kHeaderBytes + kSlotWords * 8;
 constexpr int64_t kMultiFloats = (kWorkspaceBytes - kMultiOffset) / 4;
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up
 constexpr int kMaxWorkspaces = 8;           // per device
+// The library's events only order work on one device: a device-scope
+// release on record (the default, a system-scope one, writes back caches
+// between back-to-back wide-row calls).
+constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventReleaseToDevice;
 
 struct Workspace {
     void *base = nullptr;
@@ -156,7 +160,7 @@ int new_workspace(hipStream_t stream, Workspace *w) {
         w->base = nullptr;
         return SNR_ERR_WORKSPACE;
     }
-    e = hipEventCreateWithFlags(&w->last_use, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&w->last_use, kEventFlags);
     if (e == hipSuccess)
         e = fill_words(w->base, kWorkspaceBytes / 4, 0u, stream);
     if (e != hipSuccess) {
@@ -241,20 +245,16 @@ bool split_cooperative() {
     return v && *v && std::strcmp(v, "0") != 0;
 }
 
-// The event recorded after the latest eager split-row launch on a device
-// (caller holds g_ws_mu).
-std::map<int, hipEvent_t> g_split_serial;
+// The workspace whose last_use event marks the latest eager split-row launch
+// on a device (caller holds g_ws_mu). One record per call serves both
+// orders: each record costs about 3.5 us between back-to-back calls.
+std::map<int, Workspace *> g_split_last;
 
-int split_serial_event(int dev, hipEvent_t **out) {
-    auto it = g_split_serial.find(dev);
-    if (it == g_split_serial.end()) {
-        hipEvent_t ev = nullptr;
-        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e);
-        it = g_split_serial.emplace(dev, ev).first;
-    }
-    *out = &it->second;
-    return SNR_OK;
+// Order `stream` after the work an event marks. (Also when the event was
+// recorded on `stream` itself: a destroyed stream's handle can come back as
+// a new stream's while the old stream's work still runs.)
+hipError_t wait_for(hipStream_t stream, hipEvent_t ev) {
+    return hipStreamWaitEvent(stream, ev, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -542,7 +542,8 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     } else {
         // Split-row and multi-pass launches use a workspace: the whole
         // sequence is enqueued under the workspace lock, after the wait on
-        // its previous use and before the record of this one.
+        // its previous use and before the record of this one (which also
+        // marks the device's latest split-row launch).
         // The allocation-free entry point uses its device's static scratch
         // instead, with no events (its calls must not overlap on a device).
         std::lock_guard<std::mutex> lk(g_ws_mu);
@@ -557,7 +558,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
         }
         if (rc != SNR_OK) return rc;
         if (events) {
-            hipError_t e = hipStreamWaitEvent(stream, ws->last_use, 0);
+            hipError_t e = wait_for(stream, ws->last_use);
             if (e != hipSuccess) return hip_fail(e);
         }
         hipError_t e = hipSuccess;
@@ -592,12 +593,13 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             // each be partly resident, waiting for workgroups the other
             // keeps out. (Under capture the graph's stream order is the
             // caller's to keep.)
-            hipEvent_t *prev = nullptr;
             if (events) {
-                rc = split_serial_event(dev, &prev);
-                if (rc != SNR_OK) return rc;
-                e = hipStreamWaitEvent(stream, *prev, 0);
-                if (e != hipSuccess) return hip_fail(e);
+                Workspace *prev = g_split_last[dev];
+                if (prev && prev != ws) {
+                    e = wait_for(stream, prev->last_use);
+                    if (e != hipSuccess) return hip_fail(e);
+                }
+                g_split_last[dev] = ws;   // its record below marks this launch
             }
             const bool coop = split_cooperative();
             for (int64_t r0 = 0; r0 < a.rows && e == hipSuccess; r0 += step) {
@@ -613,7 +615,6 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
                 if (e == hipSuccess)
                     e = k->split(a, sl, r0, nr, c.chunks, groups, coop, stream);
             }
-            if (e == hipSuccess && events) e = hipEventRecord(*prev, stream);
         }
         if (e == hipSuccess && events) e = hipEventRecord(ws->last_use, stream);
         if (e != hipSuccess) return hip_fail(e);
