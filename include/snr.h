@@ -195,7 +195,7 @@ SNR_API int sandwich_tail_noalloc(const float *a, const float *r,
  * stored rounded to the storage type, and y is the norm of its f32 value
  * (one rounding in y; normalising the rounded copy would add the rounding
  * of the row's largest element to every output). Rows too wide for the
- * split-row kernel (beyond about 6 million elements) go through multi-pass
+ * split-row kernel (beyond about 4.2 million elements: 1024 chunks of 4096) go through multi-pass
  * kernels whose last pass re-reads the stored h: there y carries two.
  * Same aliasing rules as sandwich_tail.
  *

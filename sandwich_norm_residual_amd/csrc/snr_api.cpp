@@ -514,7 +514,7 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
     const KernelEntry *k = c.k;
 
     if (k->kind == KIND_SPLIT) {
-        // The cooperative grid needs every chunk of a row co-resident; rows
+        // The split grid needs every chunk of a row co-resident; rows
         // wider than that go through the multi-pass kernels instead (unless
         // the split shape was forced, which then fails).
         int per_cu = 0;
