@@ -180,8 +180,9 @@ SNR_API int sandwich_tail(const float *a, const float *r, const float *gamma_pos
  * that overlaps another wide-row call there). Serialise them, e.g. on one
  * stream. The array's slots carry per-call tags, so what an earlier call
  * left there is never taken for a later call's. The first call on a device
- * looks up the array's device address and clears it with a kernel on
- * `stream`.
+ * looks up the array's device address; the first call there that is not
+ * being captured into a graph clears the array with a kernel on `stream`
+ * (a captured call clears, inside the graph, the slots its launch uses).
  */
 SNR_API int sandwich_tail_noalloc(const float *a, const float *r,
                                   const float *gamma_post, float eps_post,
@@ -380,7 +381,9 @@ SNR_API int snr_last_shape(char *buf, int len);
  * of such events counted in the workspace (current device, stream) holds,
  * and clears the count. It synchronises the stream and the workspace's last
  * use. 0 means every wait completed normally (or the stream holds no
- * workspace).
+ * workspace). Overruns of sandwich_tail_noalloc's calls are counted in its
+ * static array, which this does not read; their rows' outputs are NaN all
+ * the same.
  * The environment variable SNR_SPLIT_SPIN_LIMIT (an integer >= 0, read at
  * each split-row launch) replaces the default bound of 2^22 polls; tests use
  * 0 to make every wait give up at once. SNR_SPLIT_EPOCH (read when a

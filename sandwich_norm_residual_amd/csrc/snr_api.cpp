@@ -117,6 +117,7 @@ struct Workspace {
     uint64_t stamp = 0;             // last use, for eviction
     bool pinned = false;            // captured into a graph
     uint32_t next_tag = 1;          // the next split-row launch's tag
+    bool uncleared = false;         // static scratch not yet cleared eagerly
 };
 
 std::mutex g_ws_mu;   // guards g_ws, g_ws_clock and every workspace use
@@ -468,20 +469,29 @@ static __device__ __align__(256) unsigned char scratch[snr::kWorkspaceBytes];
 namespace snr {
 namespace {
 
-// The device address of `scratch` on device `dev`, cleared on `stream` the
-// first time (caller holds g_ws_mu; `dev` is the current device).
+// The device address of `scratch` on device `dev`, looked up on the first
+// call there, and the array cleared by the first eager call: its slots and
+// overrun count start at zero before an eager launch takes tag 1. (A call
+// recorded into a graph clears the slots its launch uses inside the graph,
+// and the multi-pass scratch is written before it is read.) Caller holds
+// g_ws_mu; `dev` is the current device.
 int setup_scratch(int dev, hipStream_t stream) {
     if (dev < 0 || dev >= kMaxScratchDevices) return SNR_ERR_DEVICE;
     Workspace &w = g_scratch_ws[dev];
-    if (w.base) return SNR_OK;
-    void *ptr = nullptr;
-    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return hip_fail(e);
-    // the slots and the overrun count start at zero
-    e = fill_words(ptr, kWorkspaceBytes / 4, 0u, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    w.base = ptr;
-    w.next_tag = 1;
+    if (!w.base) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        w.base = ptr;
+        w.next_tag = 1;
+        w.uncleared = true;
+    }
+    if (w.uncleared && !capturing(stream)) {
+        const hipError_t e = fill_words(w.base, kWorkspaceBytes / 4, 0u, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        w.uncleared = false;
+        w.next_tag = 1;
+    }
     return SNR_OK;
 }
 
