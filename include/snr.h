@@ -325,7 +325,9 @@ SNR_API int snr_last_hip_error(void);
  *                             16-bit), one workgroup per chunk, joined by a
  *                             cross-workgroup reduction through device
  *                             memory; every chunk of a row must be
- *                             co-resident (g and vpt are ignored)
+ *                             co-resident (vpt is ignored; g > 0 caps the
+ *                             rows in flight, the workgroups per chunk, so
+ *                             that each workgroup walks more rows)
  *          SNR_SHAPE_MULTIPASS rows wider than that: per-chunk partial sums,
  *                             a per-row combine and an apply pass through
  *                             device memory (reads the row twice; the tail

@@ -590,9 +590,13 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             e = k->occupancy(&per_cu);
             if (e != hipSuccess) return hip_fail(e);
             // Every workgroup of the grid must be resident at once: at most
-            // floor(capacity / chunks) rows are in flight.
-            const int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
+            // floor(capacity / chunks) rows are in flight. A forced split
+            // shape's g > 0 lowers that (each workgroup then walks more rows).
+            int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
             if (max_groups < 1) return SNR_ERR_WORKSPACE;
+            if (t_force_kind == SNR_SHAPE_SPLIT && t_force_g > 0 &&
+                t_force_g < max_groups)
+                max_groups = t_force_g;
             const SplitState st = split_state(ws->base);
             // each launch's rows x reductions x chunks slots fit the slots
             const int64_t nph = op == OP_TAIL ? 2 : 1;

@@ -95,6 +95,32 @@ def test_forced_shape(oracle, case):
         assert shape == f"multipass:256:16:{w}:3", shape
 
 
+SPLIT_PAIRS = PAIRS + [("plain", "f32"), ("plain", "bf16"), ("tail", "f32")]
+
+
+@pytest.mark.parametrize("groups,rows,chunks", [(2, 19, 3), (3, 20, 1),
+                                                (5, 23, 2)])
+@pytest.mark.parametrize("op_st", SPLIT_PAIRS, ids=lambda p: "-".join(p))
+def test_forced_split_walks_many_rows(oracle, op_st, groups, rows, chunks):
+    """The split-row kernel with its rows in flight capped (g in the forced
+    shape), so every workgroup walks 4 to 10 rows: each register ring (the
+    four row buffers, the second stream's, and the 16-bit tail's f32 h) is
+    reused several times, with uneven trip counts, on ragged rows. Every
+    output matches the oracle and no wait gives up."""
+    op, st = op_st
+    w = VEC[st]
+    nv = (chunks - 1) * (4096 // w) + 5
+    n = nv * w + w - 1
+    label = f"split-walk-{op}-{st}-g{groups}-r{rows}-n{n}"
+    say(f"{label}")
+    inp = make_inputs(op, st, rows, n, 30000 + groups * 101 + rows + n)
+    with snr.forced_shape("split", groups, 8):
+        shape = run_and_check(oracle, op, inp, label,
+                              scale=0.75 if op == "norm_add" else None)
+    assert shape == f"split:256:{4096 // (256 * w)}:{w}:{chunks}", shape
+    assert snr.split_timeouts() == 0
+
+
 @pytest.mark.parametrize("name", ["tail_4096x6656_bf16", "tail_4096x6656_f16",
                                   "norm_add_4096x6656_f32",
                                   "add_norm_4096x6656_f32"])
