@@ -325,9 +325,7 @@ SNR_API int snr_last_hip_error(void);
  *                             16-bit), one workgroup per chunk, joined by a
  *                             cross-workgroup reduction through device
  *                             memory; every chunk of a row must be
- *                             co-resident (vpt is ignored; g > 0 caps the
- *                             rows in flight, the workgroups per chunk, so
- *                             that each workgroup walks more rows)
+ *                             co-resident (g and vpt are ignored)
  *          SNR_SHAPE_MULTIPASS rows wider than that: per-chunk partial sums,
  *                             a per-row combine and an apply pass through
  *                             device memory (reads the row twice; the tail
@@ -359,6 +357,18 @@ enum {
     SNR_SHAPE_PERSIST = 4
 };
 SNR_API int snr_force_shape(int kind, int g, int vpt);
+/*
+ * snr_force_grid - diagnostics: caps the rows in flight of the kernels that
+ * walk several rows per workgroup, for subsequent calls on the calling
+ * thread: the persistent row tiles (SNR_SHAPE_PERSIST, and rmsnorm_q8_1's
+ * persistent tiles) launch at most `max_groups` workgroups, and the
+ * split-row kernels at most `max_groups` workgroups per chunk. Each
+ * workgroup then walks more rows, which exercises the kernels' pipelined
+ * loops on small inputs; results are unchanged. 0 restores the default
+ * (as many as the device holds at once); a negative value returns
+ * SNR_ERR_SHAPE.
+ */
+SNR_API int snr_force_grid(int64_t max_groups);
 SNR_API int snr_last_shape(char *buf, int len);
 
 /*

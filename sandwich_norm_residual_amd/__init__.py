@@ -340,6 +340,18 @@ def forced_shape(kind: str, g: int = 0, vpt: int = 0):
         _lib.force_shape(_lib.SHAPE_AUTO)
 
 
+@contextlib.contextmanager
+def forced_grid(max_groups: int):
+    """Cap the rows in flight (workgroups of the persistent tiles, and per
+    chunk of the split-row kernels) for calls made on this thread inside the
+    block, so each workgroup walks more rows (diagnostics and tests)."""
+    _lib.force_grid(max_groups)
+    try:
+        yield
+    finally:
+        _lib.force_grid(0)
+
+
 def last_shape() -> str:
     """"kind:g:vpt:width[:chunks]" of this thread's most recent launch
     (width = elements per 128-bit vector)."""

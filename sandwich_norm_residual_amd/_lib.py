@@ -68,6 +68,7 @@ SIGNATURES = {
     "snr_strerror": (ctypes.c_char_p, [_int]),
     "snr_last_hip_error": (_int, []),
     "snr_force_shape": (_int, [_int, _int, _int]),
+    "snr_force_grid": (_int, [_i64]),
     "snr_last_shape": (_int, [ctypes.c_char_p, _int]),
     "snr_split_timeouts": (_int, [_vp, ctypes.POINTER(_i64)]),
 }
@@ -169,6 +170,10 @@ def rmsnorm_fwd_multi(segments, n, dtype, stream) -> int:
 
 def force_shape(kind: int, g: int = 0, vpt: int = 0) -> None:
     check(lib().snr_force_shape(kind, g, vpt), "snr_force_shape")
+
+
+def force_grid(max_groups: int = 0) -> None:
+    check(lib().snr_force_grid(max_groups), "snr_force_grid")
 
 
 def last_shape() -> str:

@@ -1,8 +1,8 @@
 // snr_api.cpp - the C ABI of libsnr (declared in include/snr.h): argument
 // validation, dispatch-shape selection, the split-row workspace and the
 // kernel launches. Host code only; the kernels live in snr_kernels.hip (row
-// tiles, split rows, multi-pass), snr_persist.hip (persistent row tiles) and
-// snr_q8.hip (RMSNorm into Q8_1 records).
+// tiles, multi-pass), snr_persist.hip (persistent row tiles), snr_split.hip
+// (split rows) and snr_q8.hip (RMSNorm into Q8_1 records).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -27,12 +27,19 @@ thread_local int t_last_hip_error = 0;
 thread_local int t_force_kind = SNR_SHAPE_AUTO;
 thread_local int t_force_g = 0;
 thread_local int t_force_vpt = 0;
+thread_local int64_t t_force_grid = 0;   // snr_force_grid; 0: no cap
 thread_local char t_last_shape[64] = "";
 
 int hip_fail(hipError_t e) {
     t_last_hip_error = (int)e;
     return SNR_ERR_HIP;
 }
+
+}  // namespace
+
+int64_t forced_grid_cap() { return t_force_grid; }
+
+namespace {
 
 bool debug_enabled() {
     static const bool on = [] {
@@ -590,13 +597,12 @@ int launch(int op, int st, int64_t esize, const RowArgs &args_in,
             e = k->occupancy(&per_cu);
             if (e != hipSuccess) return hip_fail(e);
             // Every workgroup of the grid must be resident at once: at most
-            // floor(capacity / chunks) rows are in flight. A forced split
-            // shape's g > 0 lowers that (each workgroup then walks more rows).
+            // floor(capacity / chunks) rows are in flight (fewer under
+            // snr_force_grid: each workgroup then walks more rows).
             int64_t max_groups = (int64_t)per_cu * info.cus / c.chunks;
             if (max_groups < 1) return SNR_ERR_WORKSPACE;
-            if (t_force_kind == SNR_SHAPE_SPLIT && t_force_g > 0 &&
-                t_force_g < max_groups)
-                max_groups = t_force_g;
+            if (t_force_grid > 0 && t_force_grid < max_groups)
+                max_groups = t_force_grid;
             const SplitState st = split_state(ws->base);
             // each launch's rows x reductions x chunks slots fit the slots
             const int64_t nph = op == OP_TAIL ? 2 : 1;
@@ -984,6 +990,12 @@ int snr_force_shape(int kind, int g, int vpt) {
     t_force_kind = kind;
     t_force_g = g;
     t_force_vpt = vpt;
+    return SNR_OK;
+}
+
+int snr_force_grid(int64_t max_groups) {
+    if (max_groups < 0) return SNR_ERR_SHAPE;
+    t_force_grid = max_groups;
     return SNR_OK;
 }
 

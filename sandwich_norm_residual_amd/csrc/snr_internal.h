@@ -126,6 +126,10 @@ const KernelEntry *q8_kernel_table(int *count);
 const KernelEntry *persist_kernel_table(int *count);   // snr_persist.hip
 const KernelEntry *split_kernel_table(int *count);     // snr_split.hip
 
+// The calling thread's cap on rows in flight (snr_force_grid; 0: none): the
+// persistent tiles launch at most this many workgroups.
+int64_t forced_grid_cap();
+
 // Set `words` 32-bit words to `value` with a kernel (used instead of a
 // memset so that the call can also be recorded into a HIP graph).
 hipError_t fill_words(void *p, int64_t words, unsigned int value,

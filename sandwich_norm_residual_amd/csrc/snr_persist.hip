@@ -198,6 +198,8 @@ hipError_t launch_persist(const RowArgs &p, int64_t row0, int64_t nrows,
     int64_t blocks = nrows;
     const int64_t resident = resident_blocks<&persist_kernel<OP, ST, G, VPT>>(G);
     if (resident > 0 && blocks > resident) blocks = resident;
+    const int64_t cap = forced_grid_cap();
+    if (cap > 0 && blocks > cap) blocks = cap;
     hipLaunchKernelGGL((persist_kernel<OP, ST, G, VPT>), dim3((unsigned int)blocks),
                        dim3(G), 0, stream, p, row0, row0 + nrows);
     return hipGetLastError();

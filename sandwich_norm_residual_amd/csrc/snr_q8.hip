@@ -435,6 +435,8 @@ hipError_t launch_q8(const RowArgs &p, int64_t row0, int64_t nrows,
     if constexpr (q8_persistent(VPT * Codec<ST>::W)) {
         const int64_t resident = resident_blocks<&q8_kernel<ST, G, VPT>>(BLOCK);
         if (resident > 0 && blocks > resident) blocks = resident;
+        const int64_t cap = forced_grid_cap();
+        if (cap > 0 && blocks > cap) blocks = cap;
     }
     hipLaunchKernelGGL((q8_kernel<ST, G, VPT>), dim3((unsigned int)blocks),
                        dim3(BLOCK), 0, stream, p, row0, row0 + nrows);

@@ -102,8 +102,8 @@ SPLIT_PAIRS = PAIRS + [("plain", "f32"), ("plain", "bf16"), ("tail", "f32")]
                                                 (5, 23, 2)])
 @pytest.mark.parametrize("op_st", SPLIT_PAIRS, ids=lambda p: "-".join(p))
 def test_forced_split_walks_many_rows(oracle, op_st, groups, rows, chunks):
-    """The split-row kernel with its rows in flight capped (g in the forced
-    shape), so every workgroup walks 4 to 10 rows: each register ring (the
+    """The split-row kernel with its rows in flight capped (snr_force_grid),
+    so every workgroup walks 4 to 10 rows: each register ring (the
     four row buffers, the second stream's, and the 16-bit tail's f32 h) is
     reused several times, with uneven trip counts, on ragged rows. Every
     output matches the oracle and no wait gives up."""
@@ -114,7 +114,7 @@ def test_forced_split_walks_many_rows(oracle, op_st, groups, rows, chunks):
     label = f"split-walk-{op}-{st}-g{groups}-r{rows}-n{n}"
     say(f"{label}")
     inp = make_inputs(op, st, rows, n, 30000 + groups * 101 + rows + n)
-    with snr.forced_shape("split", groups, 8):
+    with snr.forced_shape("split", 0, 8), snr.forced_grid(groups):
         shape = run_and_check(oracle, op, inp, label,
                               scale=0.75 if op == "norm_add" else None)
     assert shape == f"split:256:{4096 // (256 * w)}:{w}:{chunks}", shape

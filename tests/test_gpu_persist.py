@@ -188,3 +188,28 @@ def test_automatic_choice_one_round(oracle, case):
     sub = {k: (val[pick] if isinstance(val, np.ndarray) and val.ndim == 2
                else val) for k, val in inp.items()}
     _check(oracle, op, sub, [o[pick] for o in got], label + "-sampled")
+
+
+@pytest.mark.parametrize("cap,rows", [(3, 22), (4, 21)])
+@pytest.mark.parametrize("case", _cases(),
+                         ids=lambda c: "{}-{}-g{}-v{}".format(*c))
+def test_persist_walks_many_rows(oracle, case, cap, rows):
+    """The persistent grid capped at a few workgroups (snr_force_grid), so
+    each walks 5 to 8 rows through its two row buffers (odd and even trip
+    counts, the peeled first row and the unrolled loop's tail): the same
+    bits as the row tile and the oracle's values."""
+    op, st, g, v = case
+    w = VEC[st]
+    nv = g * v - g // 2
+    n = nv * w
+    label = f"persist-walk-{op}-{st}-g{g}-v{v}-cap{cap}-r{rows}"
+    say(label)
+    inp = _inputs(op, st, rows, n, 33000 + g + v + n + cap)
+    with snr.forced_shape("persist", g, v), snr.forced_grid(cap):
+        got = _run(op, inp)
+        assert snr.last_shape() == f"persist:{g}:{v}:{w}", snr.last_shape()
+    _check(oracle, op, inp, got, label)
+    with snr.forced_shape("rowtile", g, v):
+        ref = _run(op, inp)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), label

@@ -59,6 +59,44 @@ def test_forced_shape(oracle, case):
         assert shape == f"multipass:256:16:{w}:3", shape
 
 
+def _persistent_cases():
+    # the tiles holding at most 16 values per lane run persistent
+    cases = []
+    for st in ("f32", "bf16", "f16"):
+        extra = [(1024, 16)] if st == "f32" else [(4, 4)]
+        for g, v in Q8_ROWTILE + extra:
+            if v * VEC[st] <= 16:
+                cases.append((st, g, v))
+    return cases
+
+
+@pytest.mark.parametrize("case", _persistent_cases(),
+                         ids=lambda c: "{}-g{}-v{}".format(*c))
+def test_persistent_walks_many_rows(oracle, case):
+    """The persistent Q8_1 tiles with their grid capped at three workgroups
+    (snr_force_grid), so each walks 5 or 6 row blocks (its prefetch, the
+    peeled first block and the loop's tail), the last block partly filled:
+    records equal to the uncapped launch's, and the oracle's."""
+    st, g, v = case
+    w = VEC[st]
+    bv = 32 // w
+    nv = max(bv, (g * v - g // 2) // bv * bv)
+    n = nv * w
+    rpb = 256 // g if g < 128 else 1      # rows per workgroup
+    rows = rpb * 16 + max(1, rpb // 2)    # 17 row blocks, the last partial
+    label = f"q8-walk-{st}-g{g}-v{v}-n{n}-r{rows}"
+    say(label)
+    inp = gen.random_plain(rows, n, 27000 + g * 7 + v + n, dtype=st)
+    with snr.forced_shape("rowtile", g, v), snr.forced_grid(3):
+        blocks = run_q8(inp)
+        shape = snr.last_shape()
+    assert shape == f"rowtile:{g}:{v}:{w}", shape
+    check_q8(oracle, inp, blocks, label)
+    with snr.forced_shape("rowtile", g, v):
+        ref = run_q8(inp)
+    assert np.array_equal(np.asarray(blocks), np.asarray(ref)), label
+
+
 @pytest.mark.parametrize("name", ["q8_4096x6656_f32", "q8_4096x6656_bf16",
                                   "q8_1x2560_f32", "q8_edge_256x6656_f32"])
 def test_workload_full_size(oracle, name):
