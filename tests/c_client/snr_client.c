@@ -14,6 +14,7 @@
  *   sandwich_tail(a, r, gp, eps_post, gq, eps_pre)      -> DIR/h, DIR/y
  *   rmsnorm_fwd(a, gp, eps_pre)                          -> DIR/z
  *   sandwich_tail_inplace on a copy of r                 -> DIR/hi, DIR/yi
+ *   sandwich_tail_noalloc(a, r, gp, eps_post, gq, eps_pre) -> DIR/hn, DIR/yn
  * and for bf16:
  *   sandwich_tail_typed(a, r, gp, eps_post, gq, eps_pre) -> DIR/h, DIR/y
  *   norm_then_add(a, r, gp, eps_post, no scale)          -> DIR/na
@@ -82,7 +83,8 @@ static int run_f32(int64_t rows, int64_t n, const float *eps,
     float *a = upload("a", tb), *r = upload("r", tb), *ri = upload("r", tb);
     float *gp = upload("gp", gb), *gq = upload("gq", gb);
     float *h = device(tb), *y = device(tb), *z = device(tb), *yi = device(tb);
-    if (!a || !r || !ri || !gp || !gq || !h || !y || !z || !yi)
+    float *hn = device(tb), *yn = device(tb);
+    if (!a || !r || !ri || !gp || !gq || !h || !y || !z || !yi || !hn || !yn)
         return fail("inputs or device allocation", 0);
 
     /* invalid arguments: each is refused before anything is enqueued */
@@ -99,6 +101,11 @@ static int run_f32(int64_t rows, int64_t n, const float *eps,
     if (rc != SNR_ERR_SHAPE) return fail("shape check", rc);
     rc = rmsnorm_fwd(a, gp, eps[1], 0, n, SNR_F32, z, stream);
     if (rc != SNR_OK) return fail("rows == 0 no-op", rc);
+    rc = sandwich_tail_noalloc(a, r, gp, eps[0], gq, eps[1], hn, a, rows, n,
+                               stream);
+    if (rc != SNR_ERR_ALIAS) return fail("no-alloc alias check", rc);
+    rc = snr_force_grid(-1);
+    if (rc != SNR_ERR_SHAPE) return fail("grid cap check", rc);
 
     rc = sandwich_tail(a, r, gp, eps[0], gq, eps[1], h, y, rows, n, stream);
     if (rc != SNR_OK) return fail("sandwich_tail", rc);
@@ -107,13 +114,17 @@ static int run_f32(int64_t rows, int64_t n, const float *eps,
     rc = sandwich_tail_inplace(a, ri, gp, eps[0], gq, eps[1], yi, rows, n,
                                SNR_F32, stream);
     if (rc != SNR_OK) return fail("sandwich_tail_inplace", rc);
+    rc = sandwich_tail_noalloc(a, r, gp, eps[0], gq, eps[1], hn, yn, rows, n,
+                               stream);
+    if (rc != SNR_OK) return fail("sandwich_tail_noalloc", rc);
     if (hipStreamSynchronize(stream) != hipSuccess)
         return fail("hipStreamSynchronize", 0);
     if (!download("h", h, tb) || !download("y", y, tb) ||
         !download("z", z, tb) || !download("hi", ri, tb) ||
-        !download("yi", yi, tb))
+        !download("yi", yi, tb) || !download("hn", hn, tb) ||
+        !download("yn", yn, tb))
         return fail("writing outputs", 0);
-    void *all[] = {a, r, ri, gp, gq, h, y, z, yi};
+    void *all[] = {a, r, ri, gp, gq, h, y, z, yi, hn, yn};
     for (size_t i = 0; i < sizeof all / sizeof all[0]; ++i)
         (void)hipFree(all[i]);
     return 0;

@@ -60,11 +60,13 @@ def test_f32_entry_points(oracle, tmp_path, rows, n):
     want = oracle.rmsnorm(inp["a"], inp["gamma_post"], inp["eps_pre"])
     assert plain_error(z, want) <= TOL_F32
 
-    # the in-place form runs the same kernel on the same shape
-    hi = _read(tmp_path / "hi", rows, n, "f32")
-    yi = _read(tmp_path / "yi", rows, n, "f32")
-    assert np.array_equal(hi.view(np.uint32), h.view(np.uint32))
-    assert np.array_equal(yi.view(np.uint32), y.view(np.uint32))
+    # the in-place and allocation-free forms run the same kernels on the
+    # same shape
+    for hk, yk in (("hi", "yi"), ("hn", "yn")):
+        hx = _read(tmp_path / hk, rows, n, "f32")
+        yx = _read(tmp_path / yk, rows, n, "f32")
+        assert np.array_equal(hx.view(np.uint32), h.view(np.uint32)), hk
+        assert np.array_equal(yx.view(np.uint32), y.view(np.uint32)), yk
 
 
 @pytest.mark.parametrize("rows,n", [(4, 6656), (3, 100), (2, 65536 + 8)])
