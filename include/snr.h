@@ -12,8 +12,9 @@
  *   memory each, for the partial sums of the split-row and multi-pass
  *   kernels (rows wider than 65536 elements): at most 8 per device, each
  *   bound to one stream at a time, allocated by the first such call on a
- *   stream that finds none free, kept until the process exits (so at most
- *   8 MiB per device however many streams are used). When a ninth stream
+ *   stream that finds none free, kept until snr_release_workspaces or the
+ *   end of the process (so at most 8 MiB per device however many streams
+ *   are used). When a ninth stream
  *   needs one, it takes the least recently used workspace, and its launches
  *   wait on the GPU for that workspace's last use on the other stream to
  *   finish (the library records an event after each use), so uses of one
@@ -403,6 +404,22 @@ SNR_API int snr_last_shape(char *buf, int len);
  * near 2^31 - 1 to exercise the wrap of the tag numbers.
  */
 SNR_API int snr_split_timeouts(hipStream_t stream, int64_t *count);
+
+/*
+ * snr_release_workspaces - frees the current device's workspaces (the 1 MiB
+ * blocks of device memory the split-row and multi-pass kernels use for rows
+ * wider than 65536 elements), for a caller that wants that memory back or
+ * is about to unload the library. It waits on the host for each
+ * workspace's last use, then frees it; the next wide-row call on a stream
+ * allocates one again. A workspace recorded into a HIP graph is kept (the
+ * graph may still be replayed). Returns SNR_ERR_CAPTURE, freeing nothing,
+ * if a stream that holds a workspace is being captured; do not call it
+ * while any other stream of the device is being captured either (freeing
+ * device memory is not allowed during a capture). Overrun counts not yet
+ * read with snr_split_timeouts are dropped. The allocation-free entry
+ * point's static array is not affected.
+ */
+SNR_API int snr_release_workspaces(void);
 
 #ifdef __cplusplus
 }

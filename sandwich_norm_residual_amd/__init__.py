@@ -30,7 +30,8 @@ from ._lib import SnrError
 __all__ = ["rmsnorm_fwd", "rmsnorm_fwd_multi", "sandwich_tail",
            "sandwich_tail_inplace", "norm_then_add", "add_then_norm",
            "rmsnorm_q8_1", "q8_1_fields",
-           "forced_shape", "last_shape", "split_timeouts", "SnrError"]
+           "forced_shape", "forced_grid", "last_shape", "split_timeouts",
+           "release_workspaces", "SnrError"]
 
 
 def _torch():
@@ -338,6 +339,13 @@ def forced_shape(kind: str, g: int = 0, vpt: int = 0):
         yield
     finally:
         _lib.force_shape(_lib.SHAPE_AUTO)
+
+
+def release_workspaces() -> None:
+    """Free the current device's wide-row workspaces (after their last
+    uses); the next wide-row call allocates again. Workspaces recorded into a
+    HIP graph are kept."""
+    _lib.release_workspaces()
 
 
 @contextlib.contextmanager

@@ -71,6 +71,7 @@ SIGNATURES = {
     "snr_force_grid": (_int, [_i64]),
     "snr_last_shape": (_int, [ctypes.c_char_p, _int]),
     "snr_split_timeouts": (_int, [_vp, ctypes.POINTER(_i64)]),
+    "snr_release_workspaces": (_int, []),
 }
 
 _LIB = None
@@ -170,6 +171,10 @@ def rmsnorm_fwd_multi(segments, n, dtype, stream) -> int:
 
 def force_shape(kind: int, g: int = 0, vpt: int = 0) -> None:
     check(lib().snr_force_shape(kind, g, vpt), "snr_force_shape")
+
+
+def release_workspaces() -> None:
+    check(lib().snr_release_workspaces(), "snr_release_workspaces")
 
 
 def force_grid(max_groups: int = 0) -> None:

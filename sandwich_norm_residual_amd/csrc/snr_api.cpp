@@ -217,21 +217,31 @@ int acquire_workspace(int dev, hipStream_t stream, Workspace **out,
     *eager = !cap;
     std::vector<Workspace> &pool = g_ws[dev];
     for (Workspace &w : pool)
-        if (w.stream == stream) {
+        if (w.base && w.stream == stream) {
             if (cap) w.pinned = true;
             w.stamp = ++g_ws_clock;
             *out = &w;
             return SNR_OK;
         }
     if (cap) return SNR_ERR_CAPTURE;
+    // a slot released by snr_release_workspaces, a new slot, or else the
+    // least recently used workspace
     Workspace *w = nullptr;
-    if ((int)pool.size() < kMaxWorkspaces) {
+    for (Workspace &c : pool)
+        if (!c.base) {
+            w = &c;
+            break;
+        }
+    if (!w && (int)pool.size() < kMaxWorkspaces) {
         pool.reserve(kMaxWorkspaces);   // pointers into the pool stay valid
+        pool.push_back(Workspace{});
+        w = &pool.back();
+    }
+    if (w) {
         Workspace fresh;
         const int rc = new_workspace(stream, &fresh);
         if (rc != SNR_OK) return rc;
-        pool.push_back(fresh);
-        w = &pool.back();
+        *w = fresh;
     } else {
         for (Workspace &c : pool)
             if (!c.pinned && (!w || c.stamp < w->stamp)) w = &c;
@@ -1005,6 +1015,30 @@ int snr_last_shape(char *buf, int len) {
     return SNR_OK;
 }
 
+int snr_release_workspaces(void) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find(dev);
+    if (it == g_ws.end()) return SNR_OK;
+    for (Workspace &w : it->second)
+        if (w.base && !w.pinned && capturing(w.stream)) return SNR_ERR_CAPTURE;
+    for (Workspace &w : it->second) {
+        if (!w.base || w.pinned) continue;
+        // the last use recorded on its stream; no later use is enqueued
+        // while the lock is held
+        e = hipEventSynchronize(w.last_use);
+        if (e != hipSuccess) return hip_fail(e);
+        (void)hipEventDestroy(w.last_use);
+        e = hipFree(w.base);
+        if (g_split_last[dev] == &w) g_split_last[dev] = nullptr;
+        w = Workspace{};   // an empty slot, taken again by the next need
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SNR_OK;
+}
+
 int snr_split_timeouts(hipStream_t stream, int64_t *count) {
     if (!count) return SNR_ERR_NULL;
     *count = 0;
@@ -1015,7 +1049,7 @@ int snr_split_timeouts(hipStream_t stream, int64_t *count) {
     auto it = g_ws.find(dev);
     if (it == g_ws.end()) return SNR_OK;
     for (Workspace &w : it->second) {
-        if (w.stream != stream) continue;
+        if (!w.base || w.stream != stream) continue;
         // every eager use of the workspace is recorded in last_use; graph
         // replays on the stream are covered by synchronising it
         e = hipEventSynchronize(w.last_use);
