@@ -15,6 +15,7 @@
  *   rmsnorm_fwd(a, gp, eps_pre)                          -> DIR/z
  *   sandwich_tail_inplace on a copy of r                 -> DIR/hi, DIR/yi
  *   sandwich_tail_noalloc(a, r, gp, eps_post, gq, eps_pre) -> DIR/hn, DIR/yn
+ *   snr_release_workspaces() at the end
  * and for bf16:
  *   sandwich_tail_typed(a, r, gp, eps_post, gq, eps_pre) -> DIR/h, DIR/y
  *   norm_then_add(a, r, gp, eps_post, no scale)          -> DIR/na
@@ -124,6 +125,8 @@ static int run_f32(int64_t rows, int64_t n, const float *eps,
         !download("yi", yi, tb) || !download("hn", hn, tb) ||
         !download("yn", yn, tb))
         return fail("writing outputs", 0);
+    rc = snr_release_workspaces();
+    if (rc != SNR_OK) return fail("snr_release_workspaces", rc);
     void *all[] = {a, r, ri, gp, gq, h, y, z, yi, hn, yn};
     for (size_t i = 0; i < sizeof all / sizeof all[0]; ++i)
         (void)hipFree(all[i]);
