@@ -132,11 +132,11 @@ SNR_API int rmsnorm_fwd(const void *x, const void *gamma, float eps, int64_t row
  * sandwich_tail - the fused dual-epsilon sandwich tail, f32 storage.
  *
  * Defined in "RMSNorm and the dual-epsilon sandwich" (Muser book, chapter
- * 12): section 12.2 gives the layer order (a sub-block's output is
- * post-normed before it is added to the residual stream, and the stream is
- * pre-normed before the next sub-block reads it) and section 12.4.3 the fused
- * tail that performs post-norm, residual add and the next pre-norm in one
- * dispatch with two different epsilons. Per row:
+ * 12): section 12.2 gives the layer order (each sub-block's output goes
+ * through its post-norm and then into the residual stream, whose pre-norm
+ * feeds the next sub-block) and section 12.4.3 the fused tail that does the
+ * post-norm, the residual add and the next pre-norm in a single launch, each
+ * norm with its own epsilon. Per row:
  *     h = r + gamma_post * a / sqrt(mean(a^2) + eps_post)
  *     y = gamma_pre * h / sqrt(mean(h^2) + eps_pre)
  * The model the book describes uses eps_post = 1e-8 and eps_pre = 1e-5; both
