@@ -143,6 +143,12 @@ def test_force_shape_rejects_unknown_kind(L):
     assert L.snr_last_shape(buf, 8) == _lib.SNR_OK
 
 
+def test_force_grid_rejects_a_negative_cap(L):
+    assert L.snr_force_grid(-1) == _lib.SNR_ERR_SHAPE
+    assert L.snr_force_grid(3) == _lib.SNR_OK
+    assert L.snr_force_grid(0) == _lib.SNR_OK
+
+
 R = BASE + (1 << 26)
 GQ = GAM + (1 << 20)
 
